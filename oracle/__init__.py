@@ -1,0 +1,226 @@
+"""CPU oracle for the block-quantized wire codecs (ctypes wrapper over bq_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+imports it, and it imports nothing from the GPU library.
+
+All arrays are numpy: bf16 tensors as uint16 bit patterns, INT8 payloads as
+int8, E4M3 / E8M0 bytes as uint8, scales as float32.  Functions allocate and
+return their outputs.  The C functions they wrap cite the pages they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bq_oracle.c")
+_HDR = os.path.join(_HERE, "bq_oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build() -> str:
+    """Compile ``liboracle.so`` next to its source with gcc (IEEE binary32, no contraction)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = {
+    "orc_bf16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
+    "orc_f32_to_bf16": ([ctypes.c_float], ctypes.c_uint16),
+    "orc_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
+    "orc_e4m3_decode": ([ctypes.c_uint8], ctypes.c_float),
+    "orc_e8m0_scale": ([ctypes.c_float], ctypes.c_uint8),
+    "orc_quant_i8": ([_P, _I64, _P, _P], None),
+    "orc_dequant_i8": ([_P, _P, _I64, _P], None),
+    "orc_dequant_accum_i8": ([ctypes.c_int, _P, _P, _I64, _P], None),
+    "orc_ring_hop_i8": ([_P, _P, _P, _I64, _P, _P], None),
+    "orc_ring_allreduce_i8": ([ctypes.c_int, _I64, _P, _P, _P, _P], None),
+    "orc_a2a_allreduce_i8": ([ctypes.c_int, _I64, _P, _P, _P, _P, _P], None),
+    "orc_quant_mx": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
+    "orc_dequant_mx": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64], None),
+    "orc_quant_mx_slice": ([_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
+    "orc_quant_e4m3_b128": ([_P, _I64, _P, _P], None),
+    "orc_dequant_e4m3_b128": ([_P, _P, _I64, _P], None),
+}
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        stale = (not os.path.exists(_LIB) or
+                 os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC), os.path.getmtime(_HDR)))
+        if stale:
+            build()
+        L = ctypes.CDLL(_LIB)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _ptrs(arrs):
+    arr = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    return arr
+
+
+# ---- scalars -------------------------------------------------------------
+
+def bf16_to_f32(h: int) -> float:
+    return lib().orc_bf16_to_f32(h)
+
+
+def f32_to_bf16(f: float) -> int:
+    return lib().orc_f32_to_bf16(f)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def e8m0_scale(amax: float) -> int:
+    return lib().orc_e8m0_scale(amax)
+
+
+# ---- block INT8 ------------------------------------------------------------
+
+def quant_i8(x: np.ndarray):
+    x = _c(x, np.uint16).reshape(-1)
+    q = np.empty(x.size, np.int8)
+    s = np.empty(x.size // 128, np.float32)
+    lib().orc_quant_i8(x.ctypes.data, x.size, q.ctypes.data, s.ctypes.data)
+    return q, s
+
+
+def dequant_i8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = _c(q, np.int8).reshape(-1)
+    s = _c(s, np.float32).reshape(-1)
+    assert s.size * 128 == q.size
+    y = np.empty(q.size, np.uint16)
+    lib().orc_dequant_i8(q.ctypes.data, s.ctypes.data, q.size, y.ctypes.data)
+    return y
+
+
+def dequant_accum_i8(qs, ss) -> np.ndarray:
+    qs = [_c(q, np.int8).reshape(-1) for q in qs]
+    ss = [_c(s, np.float32).reshape(-1) for s in ss]
+    n = qs[0].size
+    assert all(q.size == n for q in qs) and all(s.size * 128 == n for s in ss)
+    y = np.empty(n, np.uint16)
+    lib().orc_dequant_accum_i8(len(qs), _ptrs(qs), _ptrs(ss), n, y.ctypes.data)
+    return y
+
+
+def ring_hop_i8(q_in: np.ndarray, s_in: np.ndarray, local: np.ndarray):
+    q_in = _c(q_in, np.int8).reshape(-1)
+    s_in = _c(s_in, np.float32).reshape(-1)
+    local = _c(local, np.uint16).reshape(-1)
+    n = q_in.size
+    assert local.size == n and s_in.size * 128 == n
+    q = np.empty(n, np.int8)
+    s = np.empty(n // 128, np.float32)
+    lib().orc_ring_hop_i8(q_in.ctypes.data, s_in.ctypes.data, local.ctypes.data, n,
+                          q.ctypes.data, s.ctypes.data)
+    return q, s
+
+
+def ring_allreduce_i8(partials):
+    """Returns (q_final, s_final, outs): final payload of every chunk and each rank's bf16 output."""
+    ps = [_c(p, np.uint16).reshape(-1) for p in partials]
+    W, n = len(ps), ps[0].size
+    q = np.empty(n, np.int8)
+    s = np.empty(n // 128, np.float32)
+    outs = [np.empty(n, np.uint16) for _ in range(W)]
+    lib().orc_ring_allreduce_i8(W, n, _ptrs(ps), q.ctypes.data, s.ctypes.data, _ptrs(outs))
+    return q, s, outs
+
+
+def a2a_allreduce_i8(partials):
+    """Returns (red, q_final, s_final, outs): owner bf16 sums, broadcast payloads, outputs."""
+    ps = [_c(p, np.uint16).reshape(-1) for p in partials]
+    W, n = len(ps), ps[0].size
+    red = np.empty(n, np.uint16)
+    q = np.empty(n, np.int8)
+    s = np.empty(n // 128, np.float32)
+    outs = [np.empty(n, np.uint16) for _ in range(W)]
+    lib().orc_a2a_allreduce_i8(W, n, _ptrs(ps), red.ctypes.data, q.ctypes.data, s.ctypes.data,
+                               _ptrs(outs))
+    return red, q, s, outs
+
+
+# ---- MXFP8 -----------------------------------------------------------------
+
+def quant_mx(x: np.ndarray):
+    """x: (rows, cols) uint16 bf16 -> (values uint8 (rows, cols), e8m0 uint8 (rows, cols/32))."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    v = np.empty((rows, cols), np.uint8)
+    e = np.empty((rows, cols // 32), np.uint8)
+    lib().orc_quant_mx(x.ctypes.data, rows, cols, cols, v.ctypes.data, cols, e.ctypes.data,
+                       cols // 32)
+    return v, e
+
+
+def dequant_mx(v: np.ndarray, e: np.ndarray) -> np.ndarray:
+    v = _c(v, np.uint8)
+    e = _c(e, np.uint8)
+    rows, cols = v.shape
+    assert e.shape == (rows, cols // 32)
+    y = np.empty((rows, cols), np.uint16)
+    lib().orc_dequant_mx(v.ctypes.data, cols, e.ctypes.data, cols // 32, rows, cols,
+                         y.ctypes.data, cols)
+    return y
+
+
+def quant_mx_slice(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray) -> None:
+    """Quantize slice x (rows, cols) into v[:, col_off:col_off+cols] and e[:, col_off/32:...] in place."""
+    x = _c(x, np.uint16)
+    assert v.dtype == np.uint8 and e.dtype == np.uint8
+    assert v.flags.c_contiguous and e.flags.c_contiguous
+    rows, cols = x.shape
+    assert rows <= v.shape[0] and col_off + cols <= v.shape[1]
+    assert e.shape[1] * 32 >= v.shape[1] and e.shape[0] == v.shape[0]
+    lib().orc_quant_mx_slice(x.ctypes.data, rows, cols, cols, col_off, v.ctypes.data,
+                             v.shape[1], e.ctypes.data, e.shape[1])
+
+
+# ---- E4M3 128-block codec ----------------------------------------------------
+
+def quant_e4m3_b128(x: np.ndarray):
+    x = _c(x, np.uint16).reshape(-1)
+    v = np.empty(x.size, np.uint8)
+    s = np.empty(x.size // 128, np.float32)
+    lib().orc_quant_e4m3_b128(x.ctypes.data, x.size, v.ctypes.data, s.ctypes.data)
+    return v, s
+
+
+def dequant_e4m3_b128(v: np.ndarray, s: np.ndarray) -> np.ndarray:
+    v = _c(v, np.uint8).reshape(-1)
+    s = _c(s, np.float32).reshape(-1)
+    assert s.size * 128 == v.size
+    y = np.empty(v.size, np.uint16)
+    lib().orc_dequant_e4m3_b128(v.ctypes.data, s.ctypes.data, v.size, y.ctypes.data)
+    return y

@@ -1,0 +1,80 @@
+/*
+ * bq_oracle.h -- plain, slow, single-threaded CPU oracle for the block-quantized
+ * wire codecs.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * includes, links or calls it, and it includes nothing from the GPU library.
+ *
+ * Pages cited (the text of four web pages on block-quantized wire formats):
+ *   P1 = sparkinfer pull request #46, "feat(pcie_dma): add block-INT8 wire modes
+ *        for AG, ring, and A2A" (sections Summary, Implementation, Evidence).
+ *   P2 = sparkinfer pull request #72, "feat(pcie_dma): add INT8 and MXFP8 wire
+ *        modes" (PR body Summary / Modes, and the review comment that shows the
+ *        device helper mxfp8_scale_byte).
+ *   P4 = b12x pull request #241, "[II] Support staged MXFP8 linear inputs"
+ *        (sections Behavior, Compatibility, Validation).
+ *
+ * Conventions shared by every function:
+ *   - bf16 tensors are passed as uint16_t bit patterns;
+ *   - n is the number of values, a multiple of 128; nb = n / 128 blocks;
+ *   - all arithmetic is IEEE-754 binary32 with round-to-nearest-even, done one
+ *     operation per C statement; the library is compiled with
+ *     -ffp-contract=off -fno-fast-math on x86-64 SSE (no x87 excess precision);
+ *   - inputs must be finite (non-finite inputs are outside the contract and
+ *     abort the process).
+ */
+#ifndef BQ_ORACLE_H
+#define BQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- scalar conversions ------------------------------------------------ */
+float    orc_bf16_to_f32(uint16_t h);
+uint16_t orc_f32_to_bf16(float f);          /* round to nearest, ties to even */
+uint8_t  orc_e4m3_encode(float v);          /* OCP E4M3FN, RNE, finite saturation */
+float    orc_e4m3_decode(uint8_t code);
+uint8_t  orc_e8m0_scale(float amax);        /* MXFP8 shared-exponent byte */
+
+/* ---- block-INT8 codec (P1 Summary / Implementation) ------------------- */
+void orc_quant_i8(const uint16_t* x, int64_t n, int8_t* q, float* scale);
+void orc_dequant_i8(const int8_t* q, const float* scale, int64_t n, uint16_t* y);
+void orc_dequant_accum_i8(int nsrc, const int8_t* const* q, const float* const* scale,
+                          int64_t n, uint16_t* y);
+void orc_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* local,
+                     int64_t n, int8_t* q_out, float* s_out);
+
+/* ---- one-GPU simulation of the collectives (P1 Summary) --------------- */
+/* Ring reduce-scatter + all-gather of `world` rank partials of n values each.
+ * q_final/s_final receive the final payload of every chunk, chunk c at value
+ * offset c*n/world; out[r] receives rank r's materialized bf16 tensor. */
+void orc_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                           int8_t* q_final, float* s_final, uint16_t* const* out);
+/* Quantize-once all-to-all + broadcast.  red receives the owners' bf16 sums
+ * (shard j at offset j*n/world), q_final/s_final the broadcast payloads. */
+void orc_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                          uint16_t* red, int8_t* q_final, float* s_final,
+                          uint16_t* const* out);
+
+/* ---- MXFP8 codec (P2 Summary, P4 Behavior) ---------------------------- */
+void orc_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                  uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds);
+void orc_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
+                    int64_t rows, int64_t cols, uint16_t* y, int64_t ldy);
+void orc_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                        int64_t lds);
+
+/* ---- E4M3 128-block codec, the pre-existing format the INT8 codec
+ *      replaces (P1 Summary / Why) ------------------------------------- */
+void orc_quant_e4m3_b128(const uint16_t* x, int64_t n, uint8_t* v, float* scale);
+void orc_dequant_e4m3_b128(const uint8_t* v, const float* scale, int64_t n, uint16_t* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

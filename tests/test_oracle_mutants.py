@@ -1,0 +1,81 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case edits one line of a temporary copy of ``oracle/bq_oracle.c`` (a wrong
+constant, a wrong rounding direction, a wrong index, a wrong order, a wrong
+sign), builds it with the oracle's own flags, points the oracle wrapper at the
+mutant library and runs the named pin tests, which must fail.  Everything runs
+on the CPU; the real oracle library is restored afterwards.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = [
+    ("divisor 128 instead of 127", "#define I8_QMAX 127.0f", "#define I8_QMAX 128.0f",
+     ["test_i8_worked_examples"]),
+    ("ties away from zero in INT8 rounding", "float r = rintf(t);", "float r = roundf(t);",
+     ["test_i8_worked_examples"]),
+    ("bf16 ties away from zero", "(lo == 0x8000u && (hi & 1u))", "(lo == 0x8000u)",
+     ["test_bf16_rounding_matches_torch_structured_sweep"]),
+    ("ring chunk index off by one", "int c = mod(r - 1 - k, W);", "int c = mod(r - k, W);",
+     ["test_ring_allreduce_exact_sums_and_canonical_payload"]),
+    ("A2A sources summed in reverse order", "for (int s = 0; s < nsrc; s++) {",
+     "for (int s = nsrc - 1; s >= 0; s--) {",
+     ["test_accum_respects_array_order_and_rounds_each_product"]),
+    ("E8M0 rounds an exact power of two up", "int e = (f == 0.5f) ? k - 1 : k;", "int e = k;",
+     ["test_mx_worked_examples"]),
+    ("E4M3 ties always upward", "code = (lo % 2 == 0) ? lo : hi;", "code = hi;",
+     ["test_e4m3_encode_midpoints_and_random_fp32"]),
+    ("hop subtracts the local partial", "sum[i] = deq + loc;", "sum[i] = deq - loc;",
+     ["test_ring_hop_bruteforce_and_identities"]),
+    ("zero block stores scale 1", "*scale = 0.0f;", "*scale = 1.0f;",
+     ["test_i8_worked_examples"]),
+    ("MX dequant exponent sign flipped", "float val = ldexpf(orc_e4m3_decode(v[r * ldv + c]), e);",
+     "float val = ldexpf(orc_e4m3_decode(v[r * ldv + c]), -e);",
+     ["test_mx_dequant_matches_torch_decode"]),
+    ("E4M3-b128 divides by 127", "float s = amax / E4M3_MAX;", "float s = amax / I8_QMAX;",
+     ["test_e4m3_b128_worked_examples"]),
+    ("A2A requantizes only the first shard", "for (int j = 0; j < W; j++) {\n        for (int s = 0; s < W; s++) {",
+     "for (int j = 0; j < 1; j++) {\n        for (int s = 0; s < W; s++) {",
+     ["test_a2a_requantizes_the_bf16_sum"]),
+]
+
+
+@pytest.fixture
+def mutant_lib(tmp_path, monkeypatch):
+    src = open(oracle._SRC).read()
+
+    def build(old: str, new: str) -> None:
+        assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+        d = tmp_path / "m"
+        d.mkdir(exist_ok=True)
+        (d / "bq_oracle.h").write_text(open(oracle._HDR).read())
+        (d / "bq_oracle.c").write_text(src.replace(old, new))
+        so = d / "liboracle_mutant.so"
+        subprocess.run(["gcc", *oracle.CFLAGS, str(d / "bq_oracle.c"), "-o", str(so), "-lm"],
+                       check=True)
+        monkeypatch.setattr(oracle, "_LIB", str(so))
+        monkeypatch.setattr(oracle, "_SRC", str(d / "bq_oracle.c"))
+        monkeypatch.setattr(oracle, "_HDR", str(d / "bq_oracle.h"))
+        monkeypatch.setattr(oracle, "_lib", None)
+
+    yield build
+    oracle._lib = None
+
+
+@pytest.mark.parametrize("desc,old,new,tests", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(mutant_lib, desc, old, new, tests, tmp_path):
+    mutant_lib(old, new)
+    for name in tests:
+        fn = getattr(pins, name)
+        kwargs = {}
+        if "W" in fn.__code__.co_varnames[: fn.__code__.co_argcount]:
+            kwargs["W"] = 4
+        with pytest.raises(AssertionError):
+            fn(**kwargs)

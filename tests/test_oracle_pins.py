@@ -1,0 +1,546 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests compares the oracle with itself.  The pins are:
+  * worked examples derived by hand from the pages' rules (tests/golden/);
+  * an exact-rational brute force written independently (tests/bruteforce.py);
+  * library routines for the special cases that reduce to them (torch's
+    round-to-nearest-even bf16 and E4M3FN conversions);
+  * closed forms, exhaustive sweeps and invariants (half-step bound, zero
+    blocks, canonical payload, ring/A2A sums that are exact by construction).
+"""
+from __future__ import annotations
+
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import bruteforce as bf
+import goldens
+import oracle
+import workloads
+
+
+def f32(bits_u16: np.ndarray) -> np.ndarray:
+    return (bits_u16.astype(np.uint32) << 16).view(np.float32)
+
+
+def all_finite_bf16() -> np.ndarray:
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return h[((h >> 7) & 0xFF) != 0xFF]
+
+
+# ---------------------------------------------------------------------------------------
+# scalar conversions
+# ---------------------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_structured_sweep():
+    """Every bf16 upper half with the interesting lower halves (exact, just above, just
+    below and exactly at the tie, both parities) against torch's RNE conversion."""
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    hi = np.arange(65536, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]
+    bits = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    vals = bits.view(np.float32)
+    want = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    L = oracle.lib()
+    got = np.fromiter((L.orc_f32_to_bf16(float(v)) for v in vals), dtype=np.uint16, count=vals.size)
+    finite_in = np.isfinite(vals)
+    assert np.array_equal(got[finite_in], want[finite_in])
+
+
+def test_bf16_rounding_matches_exact_nearest_even():
+    rng = random.Random(11)
+    L = oracle.lib()
+    for _ in range(3000):
+        bits = rng.getrandbits(32)
+        if (bits >> 23) & 0xFF == 0xFF:
+            continue
+        v = np.array([bits], np.uint32).view(np.float32)[0]
+        want = bf.fraction_to_bf16_bits(Fraction(float(v))) if abs(float(v)) < 3.38e38 else None
+        if want is None:
+            continue
+        got = L.orc_f32_to_bf16(float(v))
+        if float(v) == 0.0:
+            assert got & 0x7FFF == 0
+            continue
+        assert got == want, hex(bits)
+
+
+def test_e4m3_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    for c in range(256):
+        got = oracle.e4m3_decode(c)
+        ref = bf.e4m3_value(c)
+        if ref is None:
+            assert np.isnan(got) and np.isnan(want[c])
+            continue
+        assert Fraction(got) == ref and got == want[c], c
+    # closed forms of the format: largest finite, smallest normal, smallest subnormal, one
+    assert oracle.e4m3_decode(0x7E) == 448.0
+    assert oracle.e4m3_decode(0x08) == 2.0 ** -6
+    assert oracle.e4m3_decode(0x01) == 2.0 ** -9
+    assert oracle.e4m3_decode(0x38) == 1.0
+
+
+def _torch_e4m3_saturating(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.clip(v, -448.0, 448.0).astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_all_bf16_inputs_match_torch():
+    h = all_finite_bf16()
+    vals = f32(h)
+    L = oracle.lib()
+    got = np.fromiter((L.orc_e4m3_encode(float(v)) for v in vals), dtype=np.uint8, count=vals.size)
+    want = _torch_e4m3_saturating(vals)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_encode_midpoints_and_random_fp32():
+    L = oracle.lib()
+    mags = sorted(float(bf.e4m3_value(c)) for c in range(0x7F))
+    probes = []
+    for a, b in zip(mags[:-1], mags[1:]):
+        m = np.float32((a + b) / 2)
+        for d in (-1, 0, 1):
+            probes.append(np.nextafter(m, np.float32(np.inf)) if d > 0 else
+                          (np.nextafter(m, np.float32(-np.inf)) if d < 0 else m))
+    rng = np.random.default_rng(5)
+    probes = np.array(probes, np.float32)
+    rand = (rng.standard_normal(40000) * np.exp(rng.uniform(-14, 7, 40000))).astype(np.float32)
+    vals = np.concatenate([probes, -probes, rand, np.array([448, 449, 463.99, 464, 480, 1e30, -1e30,
+                                                           2.0 ** -10, 2.0 ** -149], np.float32)])
+    got = np.fromiter((L.orc_e4m3_encode(float(v)) for v in vals), dtype=np.uint8, count=vals.size)
+    assert np.array_equal(got, _torch_e4m3_saturating(vals))
+    # brute-force nearest search on a subsample (independent of torch)
+    for v in list(vals[:200]) + list(rand[:200]):
+        assert L.orc_e4m3_encode(float(v)) == bf.e4m3_nearest(Fraction(float(v)),
+                                                              negative_zero=np.signbit(v))
+
+
+def test_e4m3_encode_signed_zero_and_saturation():
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    assert oracle.e4m3_encode(0.0) == 0x00
+    assert oracle.e4m3_encode(464.0) == 0x7E        # torch would give NaN here; we saturate
+    assert oracle.e4m3_encode(-1e30) == 0xFE
+    assert oracle.e4m3_encode(-(2.0 ** -11)) == 0x80
+
+
+def test_e8m0_exhaustive_over_bf16_amax():
+    """Smallest power of two >= fl32(amax/448) by brute force, for every positive finite
+    bf16 amax, and the closed form for amax = m * 2^k: e = k - 8 + [m > 1.75]."""
+    h = all_finite_bf16()
+    h = h[(h > 0) & (h < 0x8000)]
+    amax = f32(h)
+    d = (amax / np.float32(448.0)).astype(np.float64)       # IEEE binary32 division
+    e = np.full(d.shape, 200, np.int64)
+    for k in range(127, -128, -1):
+        e = np.where(2.0 ** k >= d, k, e)
+    e = np.where(e == 200, 127, e)                            # (never hit for bf16 amax)
+    want = (e + 127).astype(np.uint8)
+    L = oracle.lib()
+    got = np.fromiter((L.orc_e8m0_scale(float(a)) for a in amax), dtype=np.uint8, count=amax.size)
+    assert np.array_equal(got, want)
+    # closed form where no clamping happens
+    m, k = np.frexp(amax.astype(np.float64))   # amax = m 2^k, m in [0.5, 1)
+    sig, ex = m * 2, k - 1                      # significand in [1, 2)
+    closed = ex - 8 + (sig > 1.75)
+    ok = (closed >= -127) & (closed <= 127)
+    assert np.array_equal(got[ok].astype(np.int64) - 127, closed[ok])
+    assert oracle.e8m0_scale(0.0) == 127        # the page's all-zero rule
+
+
+def test_e8m0_fp32_amax_bruteforce():
+    rng = random.Random(3)
+    L = oracle.lib()
+    for _ in range(400):
+        a = abs(np.float32(rng.lognormvariate(0, 30)))
+        if not np.isfinite(a) or a == 0:
+            continue
+        assert L.orc_e8m0_scale(float(a)) == bf.e8m0_byte(Fraction(float(a)))
+
+
+# ---------------------------------------------------------------------------------------
+# block INT8
+# ---------------------------------------------------------------------------------------
+
+def test_i8_worked_examples():
+    for rec in goldens.read("i8_worked.txt"):
+        x = goldens.padded_block(rec["x"], 128)
+        q, s = oracle.quant_i8(x)
+        want_scale = np.array([goldens.hexint(rec["scale"][0])], np.uint32).view(np.float32)
+        assert s.view(np.uint32)[0] == want_scale.view(np.uint32)[0], rec["name"]
+        want_q = np.zeros(128, np.int8)
+        want_q[:len(rec["q"])] = [int(t) for t in rec["q"]]
+        assert np.array_equal(q, want_q), rec["name"]
+        y = oracle.dequant_i8(q, s)
+        want_y = np.zeros(128, np.uint16)
+        want_y[:len(rec["y"])] = [goldens.hexint(t) for t in rec["y"]]
+        assert np.array_equal(y, want_y), rec["name"]
+
+
+def _bf_quant(x_bits: np.ndarray):
+    qs, ss = [], []
+    for b in range(x_bits.size // 128):
+        xs = [bf.bf16_bits_to_fraction(int(h)) for h in x_bits[b * 128:(b + 1) * 128]]
+        q, s = bf.quant_i8_block(xs)
+        qs += q
+        ss.append(s)
+    return np.array(qs, np.int8), ss
+
+
+def test_i8_quant_bruteforce_tiny():
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        x = workloads.rows(7 if trial % 2 else 6, trial, 0, 1, 384)[0]
+        if trial == 2:     # exact ties: power-of-two scale and half-integer multiples
+            x = np.zeros(384, np.uint16)
+            vals = np.float32(rng.integers(-254, 255, 384) / 2.0)
+            vals[0] = 127.0
+            x = (vals.view(np.uint32) >> 16).astype(np.uint16)
+        q, s = oracle.quant_i8(x)
+        wq, ws = _bf_quant(x)
+        assert np.array_equal(q, wq)
+        assert [Fraction(float(v)) for v in s] == ws
+        y = oracle.dequant_i8(q, s)
+        wy = [bf.dequant_i8_value(int(q[i]), ws[i // 128]) for i in range(x.size)]
+        assert np.array_equal(y, np.array(wy, np.uint16))
+
+
+def test_i8_scale_is_correctly_rounded_amax_over_127():
+    """scale is the binary32 value nearest amax/127 (checked with exact rationals)."""
+    h = all_finite_bf16()
+    h = h[(h > 0) & (h < 0x8000)][::7]
+    L = oracle.lib()
+    for hb in h:
+        x = np.zeros(128, np.uint16)
+        x[5] = hb
+        _, s = oracle.quant_i8(x)
+        amax = bf.bf16_bits_to_fraction(int(hb))
+        assert Fraction(float(s[0])) == bf.rn32(amax / 127)
+
+
+def test_i8_invariants_on_cfg1_tensor():
+    x = workloads.tensor(1, 0)
+    q, s = oracle.quant_i8(x)
+    xf = f32(x.reshape(-1)).astype(np.float64).reshape(-1, 128)
+    qb = q.astype(np.int64).reshape(-1, 128)
+    zero = np.all(xf == 0, axis=1)
+    assert 0.01 < zero.mean() < 0.03                      # ~2% zero blocks by construction
+    assert np.all(s[zero] == 0) and np.all(qb[zero] == 0)
+    assert np.all(s[~zero] > 0)
+    assert np.abs(qb).max() <= 127 and not np.any(qb == -128)
+    assert np.all(np.abs(qb[~zero]).max(axis=1) == 127)   # the amax element maps to +-127
+    # half-quantization-step bound, relative to the stored scale
+    err = np.abs(xf - qb * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -16))
+    # materialized bf16: half step plus half a bf16 ulp
+    y = f32(oracle.dequant_i8(q, s)).astype(np.float64).reshape(-1, 128)
+    ulp = np.spacing(np.abs(y).astype(np.float32)).astype(np.float64) * 2 ** 16
+    assert np.all(np.abs(xf - y) <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -16) + ulp / 2)
+    # 132-byte layout: n payload bytes plus 4 scale bytes per block
+    assert q.nbytes + s.nbytes == 132 * (x.size // 128)
+
+
+def test_i8_dequant_matches_torch_products():
+    """bf16(fl32(q*scale)) for every q and a spread of scales, against torch's IEEE
+    product and RNE bf16 conversion."""
+    rng = np.random.default_rng(1)
+    scales = np.concatenate([rng.lognormal(0, 8, 200).astype(np.float32),
+                             np.array([1.0, 2.0 ** -140, 2.0 ** -126, 3.0e36], np.float32)])
+    qv = np.arange(-127, 128, dtype=np.int8)
+    for sc in scales:
+        q = np.resize(qv, 256).astype(np.int8)
+        s = np.full(2, sc, np.float32)
+        got = oracle.dequant_i8(q, s)
+        want = (torch.from_numpy(q.astype(np.float32)) * float(sc)).to(torch.bfloat16)
+        assert np.array_equal(got, want.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_accum_single_source_is_dequant_and_zero_sources_are_neutral():
+    x = workloads.rows(7, 0, 0, 2, 1024).reshape(-1)
+    q, s = oracle.quant_i8(x)
+    assert np.array_equal(oracle.dequant_accum_i8([q], [s]), oracle.dequant_i8(q, s))
+    zq, zs = oracle.quant_i8(np.zeros_like(x))
+    assert np.array_equal(oracle.dequant_accum_i8([zq, q, zq], [zs, s, zs]), oracle.dequant_i8(q, s))
+
+
+def test_accum_respects_array_order_and_rounds_each_product():
+    """Source order is part of the definition: (a - a) + b differs from a + b - a when b
+    is absorbed by a.  And each product is rounded before the add (no FMA)."""
+    n = 128
+    q = [np.zeros(n, np.int8) for _ in range(3)]
+    s = [np.ones(1, np.float32) for _ in range(3)]
+    q[0][0], s[0][0] = 127, 2.0 ** 20
+    q[1][0], s[1][0] = -127, 2.0 ** 20
+    q[2][0], s[2][0] = 1, 2.0 ** -10
+    assert oracle.dequant_accum_i8(q, s)[0] == 0x3A80                            # 2^-10
+    assert oracle.dequant_accum_i8([q[0], q[2], q[1]], [s[0], s[2], s[1]])[0] == 0  # absorbed
+    # product rounding: 3 * (1 + 2^-23) = 3 + 3*2^-23 rounds to 3 + 2^-21 (tie to even);
+    # adding -3 then leaves exactly 2^-21, while a fused multiply-add would leave 3*2^-23.
+    q2 = [np.zeros(n, np.int8), np.zeros(n, np.int8)]
+    s2 = [np.array([np.float32(1 + 2.0 ** -23)], np.float32), np.array([1.0], np.float32)]
+    q2[0][0], q2[1][0] = 3, -3
+    got = oracle.dequant_accum_i8(q2, s2)[0]
+    assert got == bf.fraction_to_bf16_bits(Fraction(2) ** -21)
+    # brute force on random small cases
+    rng = np.random.default_rng(4)
+    for W in (1, 2, 3):
+        xs = [workloads.rows(7, r, 0, 1, 256)[0] for r in range(W)]
+        qs, ss = zip(*[oracle.quant_i8(x) for x in xs])
+        got = oracle.dequant_accum_i8(list(qs), list(ss))
+        for i in rng.integers(0, 256, 40):
+            want = bf.accum_value([int(qq[i]) for qq in qs],
+                                  [Fraction(float(sv[i // 128])) for sv in ss])
+            assert got[i] == want
+
+
+def test_ring_hop_bruteforce_and_identities():
+    for trial in range(3):
+        x = workloads.rows(6, trial, 0, 1, 256)[0]
+        loc = workloads.rows(7, trial + 10, 0, 1, 256)[0]
+        q, s = oracle.quant_i8(x)
+        q2, s2 = oracle.ring_hop_i8(q, s, loc)
+        for b in range(2):
+            wq, ws = bf.hop_block([int(v) for v in q[b * 128:(b + 1) * 128]],
+                                  Fraction(float(s[b])),
+                                  [int(h) for h in loc[b * 128:(b + 1) * 128]])
+            assert list(q2[b * 128:(b + 1) * 128]) == wq
+            assert Fraction(float(s2[b])) == ws
+    # local == 0, power-of-two scale and max |q| = 127: the hop is the identity
+    q = np.random.default_rng(0).integers(-127, 128, 256).astype(np.int8)
+    q[3], q[200] = 127, -127
+    s = np.array([2.0 ** -3, 2.0 ** 5], np.float32)
+    q2, s2 = oracle.ring_hop_i8(q, s, np.zeros(256, np.uint16))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    # local == -dequant(payload) exactly: the block sums to zero -> zero block
+    loc = (np.float32(q[:128]) * np.float32(2.0 ** -3)).astype(np.float32)
+    negloc = ((-loc).view(np.uint32) >> 16).astype(np.uint16)
+    q3, s3 = oracle.ring_hop_i8(q[:128].copy(), s[:1].copy(), negloc)
+    assert s3[0] == 0 and not q3.any()
+
+
+def _chain_position(r: int, c: int, W: int) -> int:
+    return (r - c - 1) % W
+
+
+def _exact_ring_partials(W: int, blocks_per_chunk: int, seed: int):
+    """Partials whose every ring stage is exact under the chunk schedule (chunk c starts at
+    rank c+1 and collects c+2, ...): a pilot element per block makes the running amax
+    127 * 2^j at chain position j, and the other elements are small multiples of 2^W so
+    that every quantization is exact.  The ring result must equal the exact sum."""
+    rng = np.random.default_rng(seed)
+    m = blocks_per_chunk * 128
+    n = W * m
+    parts = []
+    for r in range(W):
+        v = (rng.integers(-3, 4, n) * 2.0 ** W).astype(np.float64)
+        for c in range(W):
+            pos = _chain_position(r, c, W)
+            pilot = 127.0 if pos == 0 else 127.0 * 2.0 ** (pos - 1)
+            v[c * m: (c + 1) * m: 128] = pilot
+        parts.append(v)
+    return parts
+
+
+def _to_bf16_exact(v: np.ndarray) -> np.ndarray:
+    b = v.astype(np.float32).view(np.uint32)
+    assert not np.any(b & 0xFFFF)
+    return (b >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_ring_allreduce_exact_sums_and_canonical_payload(W):
+    parts = _exact_ring_partials(W, 2, W)
+    exact = np.sum(parts, axis=0)
+    pb = [_to_bf16_exact(p) for p in parts]
+    qf, sf, outs = oracle.ring_allreduce_i8(pb)
+    assert np.array_equal(f32(outs[0]).astype(np.float64), exact)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])          # every rank bit-identical
+    assert np.array_equal(outs[0], oracle.dequant_i8(qf, sf))   # owner uses the same payload
+
+
+def test_ring_allreduce_error_bound_and_schedule_on_random_data():
+    W = 4
+    parts = [workloads.rows(2, r, 0, 4, 512).reshape(-1) for r in range(W)]
+    qf, sf, outs = oracle.ring_allreduce_i8(parts)
+    exact = np.sum([f32(p).astype(np.float64) for p in parts], axis=0)
+    y = f32(outs[0]).astype(np.float64)
+    # each of the W quantizations of a block adds at most half its own step; the
+    # final step scale is known; bound the earlier steps by the final-amax-based scale
+    # of the partial sums computed in float64 (plus slack for fp32 sums and bf16)
+    m = exact.size // W
+    worst = np.zeros(exact.size // 128)
+    for c in range(W):
+        run = np.zeros(m)
+        order = [(c + 1 + k) % W for k in range(W)]
+        for r in order:
+            run = run + f32(parts[r][c * m:(c + 1) * m]).astype(np.float64)
+            worst[c * m // 128:(c + 1) * m // 128] += np.abs(run).reshape(-1, 128).max(1) / 127 / 2 * 1.05
+    bound = np.repeat(worst, 128) + np.abs(y) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(y - exact) <= bound)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    # schedule pin: with W=2, chunk 0 is quantized by rank 1 and hopped by rank 0
+    q1, s1 = oracle.quant_i8(parts[1][: parts[1].size // 2])
+    qh, sh = oracle.ring_hop_i8(q1, s1, parts[0][: parts[0].size // 2])
+    qf2, sf2, _ = oracle.ring_allreduce_i8(parts[:2])
+    assert np.array_equal(qf2[: qh.size], qh) and np.array_equal(sf2[: sh.size], sh)
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_a2a_allreduce_exact_sums(W):
+    """Pilot 127 per block in every source keeps each source scale 1 * 2^0 and the owner
+    sum's amax 127 W; other elements are multiples of W, so every step is exact."""
+    rng = np.random.default_rng(W)
+    n = W * 256
+    parts = []
+    for r in range(W):
+        v = (rng.integers(-2, 3, n) * float(W)).astype(np.float64)
+        v[::128] = 127.0
+        parts.append(v)
+    exact = np.sum(parts, axis=0)
+    red, qf, sf, outs = oracle.a2a_allreduce_i8([_to_bf16_exact(p) for p in parts])
+    assert np.array_equal(f32(red).astype(np.float64), exact)
+    assert np.array_equal(f32(outs[0]).astype(np.float64), exact)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.array_equal(outs[0], oracle.dequant_i8(qf, sf))
+
+
+def test_a2a_requantizes_the_bf16_sum():
+    """The broadcast payload is the block-INT8 quantization of the owner's bf16 sum."""
+    W = 4
+    parts = [workloads.rows(3, r, 0, 2, 1024).reshape(-1) for r in range(W)]
+    red, qf, sf, outs = oracle.a2a_allreduce_i8(parts)
+    q, s = oracle.quant_i8(red)
+    assert np.array_equal(q, qf) and np.array_equal(s, sf)
+    m = parts[0].size // W
+    for j in range(W):
+        qs, ss = zip(*[oracle.quant_i8(p) for p in parts])
+        got = oracle.dequant_accum_i8([qq[j * m:(j + 1) * m] for qq in qs],
+                                      [sv[j * m // 128:(j + 1) * m // 128] for sv in ss])
+        assert np.array_equal(got, red[j * m:(j + 1) * m])
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP8
+# ---------------------------------------------------------------------------------------
+
+def test_mx_worked_examples():
+    for rec in goldens.read("mx_worked.txt"):
+        x = goldens.padded_block(rec["x"], 32).reshape(1, 32)
+        v, e = oracle.quant_mx(x)
+        assert e[0, 0] == int(rec["byte"][0]), rec["name"]
+        want = np.zeros(32, np.uint8)
+        want[:len(rec["v"])] = [goldens.hexint(t) for t in rec["v"]]
+        assert np.array_equal(v[0], want), rec["name"]
+
+
+def test_mx_quant_bruteforce_rows():
+    x = workloads.rows(4, 0, 0, 3, 256)        # gains spread the scales over many octaves
+    v, e = oracle.quant_mx(x)
+    for r in range(3):
+        for g in range(8):
+            grp = [bf.bf16_bits_to_fraction(int(h)) for h in x[r, g * 32:(g + 1) * 32]]
+            byte = bf.e8m0_byte(max(abs(t) for t in grp))
+            assert e[r, g] == byte
+            sc = Fraction(2) ** (byte - 127)
+            for i, t in enumerate(grp):
+                neg0 = t == 0 and (x[r, g * 32 + i] & 0x8000) != 0
+                assert v[r, g * 32 + i] == bf.e4m3_nearest(bf.rn32(t / sc), negative_zero=neg0)
+
+
+def test_mx_never_saturates_and_bounds_error():
+    x = workloads.tensor(4, 1, nrows=64)
+    v, e = oracle.quant_mx(x)
+    dec = torch.from_numpy(v.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    scale = 2.0 ** (e.astype(np.float64) - 127)
+    xv = f32(x).astype(np.float64)
+    recon = dec * np.repeat(scale, 32, axis=1)
+    # E4M3 half-ulp bound: 2^-4 relative for normals, 2^-10 absolute (times scale) below
+    err = np.abs(xv - recon)
+    tol = np.maximum(np.abs(xv) * 2.0 ** -4, 2.0 ** -10 * np.repeat(scale, 32, axis=1))
+    assert np.all(err <= tol)
+    amax = np.abs(xv).reshape(64, -1, 32).max(2)
+    assert np.all(amax / scale <= 448.0)               # the +inf-rounded scale leaves headroom
+    assert not np.any((v & 0x7F) == 0x7F)              # no NaN codes
+
+
+def test_mx_dequant_matches_torch_decode():
+    x = workloads.tensor(4, 2, nrows=32)
+    v, e = oracle.quant_mx(x)
+    y = oracle.dequant_mx(v, e)
+    dec = torch.from_numpy(v.copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    sc = torch.from_numpy(np.repeat(e, 32, axis=1).astype(np.int32) - 127)
+    want = torch.ldexp(dec, sc.to(torch.float32)).to(torch.bfloat16)
+    assert np.array_equal(y, want.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_mx_slices_equal_concatenation_and_leave_the_rest_untouched():
+    slices = [workloads.rows(4, j, 0, 8, 384) for j in range(3)]
+    cat = np.concatenate(slices, axis=1)
+    v_all, e_all = oracle.quant_mx(cat)
+    cap, total = 12, 3 * 384
+    v = np.full((cap, total), 0xA5, np.uint8)
+    e = np.full((cap, total // 32), 0x5A, np.uint8)
+    for j, sl in enumerate(slices):
+        oracle.quant_mx_slice(sl, 384 * j, v, e)
+    assert np.array_equal(v[:8], v_all) and np.array_equal(e[:8], e_all)
+    assert np.all(v[8:] == 0xA5) and np.all(e[8:] == 0x5A)
+
+
+# ---------------------------------------------------------------------------------------
+# E4M3 128-block comparison codec
+# ---------------------------------------------------------------------------------------
+
+def test_e4m3_b128_worked_examples():
+    for rec in goldens.read("e4m3_b128_worked.txt"):
+        x = goldens.padded_block(rec["x"], 128)
+        v, s = oracle.quant_e4m3_b128(x)
+        assert s.view(np.uint32)[0] == goldens.hexint(rec["scale"][0]), rec["name"]
+        want = np.zeros(128, np.uint8)
+        want[:len(rec["v"])] = [goldens.hexint(t) for t in rec["v"]]
+        assert np.array_equal(v, want), rec["name"]
+
+
+def test_e4m3_b128_bruteforce_and_dequant():
+    x = workloads.rows(5, 0, 0, 1, 512)[0]
+    v, s = oracle.quant_e4m3_b128(x)
+    for b in range(4):
+        xs = [bf.bf16_bits_to_fraction(int(h)) for h in x[b * 128:(b + 1) * 128]]
+        amax = max(abs(t) for t in xs)
+        if amax == 0:
+            assert s[b] == 0 and not v[b * 128:(b + 1) * 128].any()
+            continue
+        sc = bf.rn32(amax / 448)
+        assert Fraction(float(s[b])) == sc
+        for i, t in enumerate(xs[:64]):
+            neg0 = t == 0 and (x[b * 128 + i] & 0x8000) != 0
+            assert v[b * 128 + i] == bf.e4m3_nearest(bf.rn32(t / sc), negative_zero=neg0)
+    y = oracle.dequant_e4m3_b128(v, s)
+    dec = torch.from_numpy(v.copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    want = (dec * torch.from_numpy(np.repeat(s, 128))).to(torch.bfloat16)
+    assert np.array_equal(y, want.view(torch.int16).numpy().view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------------
+# layout figures the pages print
+# ---------------------------------------------------------------------------------------
+
+def test_layout_figures_from_the_pages():
+    kv = goldens.read_kv("layout.txt")
+    n = 128 * 56
+    x = workloads.rows(6, 0, 0, 1, n)[0]
+    q, s = oracle.quant_i8(x)
+    assert (q.nbytes + s.nbytes) // (n // 128) == int(kv["bytes_per_block_i8"])
+    v, e = oracle.quant_mx(x.reshape(1, -1))
+    assert (v.nbytes + e.nbytes) // (n // 128) == int(kv["bytes_per_128_mx"])
+    assert x.nbytes // (n // 128) == int(kv["bytes_per_128_bf16"])
+    cut = 100.0 * (1 - int(kv["bytes_per_block_i8"]) / int(kv["bytes_per_128_bf16"]))
+    assert round(cut, 1) == float(kv["wire_reduction_percent_1dp"])
