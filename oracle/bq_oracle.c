@@ -139,7 +139,8 @@ uint8_t orc_e8m0_scale(float amax) {
 
 /* One 128-value block of binary32 values -> 128 signed bytes + FP32 scale.
  * amax = max |x|; scale = amax / 127; q = round-half-even(x / scale) clamped
- * to [-127, 127]; an all-zero block stores scale 0 and payload 0. */
+ * to [-127, 127]; an all-zero block stores scale 0 and payload 0 (P1 Summary and
+ * Implementation give the rule and the zero-block case). */
 static void quant_block_f32(const float* x, int8_t* q, float* scale) {
     float amax = 0.0f;
     for (int i = 0; i < BLK; i++) {
@@ -148,13 +149,16 @@ static void quant_block_f32(const float* x, int8_t* q, float* scale) {
         if (a > amax)
             amax = a;
     }
-    if (amax == 0.0f) {
+    float s = amax / I8_QMAX;
+    /* A nonzero amax below 127 * 2^-150 gives a scale that rounds to 0; only binary32
+     * sums (a ring hop) can reach it.  Such a block dequantizes to 0 whatever its
+     * payload, so it is stored exactly like an all-zero block. */
+    if (amax == 0.0f || s == 0.0f) {
         *scale = 0.0f;
         for (int i = 0; i < BLK; i++)
             q[i] = 0;
         return;
     }
-    float s = amax / I8_QMAX;
     *scale = s;
     for (int i = 0; i < BLK; i++) {
         float t = x[i] / s;

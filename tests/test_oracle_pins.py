@@ -324,6 +324,18 @@ def test_ring_hop_bruteforce_and_identities():
     assert s3[0] == 0 and not q3.any()
 
 
+def test_ring_hop_scale_underflow_is_a_zero_block():
+    """A binary32 hop sum with 0 < amax < 127 * 2^-150 has a scale that rounds to 0; the
+    block is stored as a zero block (scale 0, payload 0), which dequantizes to the same
+    zeros as any payload would with that scale."""
+    q = np.zeros(128, np.int8)
+    q[7] = 1
+    s = np.array([2.0 ** -149], np.float32)        # smallest subnormal binary32
+    q2, s2 = oracle.ring_hop_i8(q, s, np.zeros(128, np.uint16))
+    assert s2[0] == 0 and not q2.any()
+    assert bf.rn32(Fraction(2) ** -149 / 127) == 0  # the scale really underflows
+
+
 def _chain_position(r: int, c: int, W: int) -> int:
     return (r - c - 1) % W
 
