@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized wire codec path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input: four
+simulated ranks, each holding a 3072x7168 bf16 partial (N(0, 0.5)), go through
+  * the i8_ring all-reduce: block-INT8 quantize, three fused ring-hop steps, and
+    every rank's materialization from the final payloads;
+  * the i8_a2a all-reduce: quantize once, 4-source FP32 accumulate per owner,
+    requantize, every rank's materialization;
+  * MXFP8: the four partials staged as 128-aligned slices of a 3072x28672 buffer,
+    then dequantized;
+  * the E4M3 128-block codec on rank 0's partial, quantize and dequantize.
+`value` is the algorithmic bytes of the step (each kernel's inputs read once and
+outputs written once) over the step time, in GB/s; HBM peak is 8 TB/s.  Inputs are
+resident in HBM; several input sets rotate so that the 256 MB last-level cache
+cannot hold them between uses.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) for i8 quant + ring-hop at 3072×7168 bf16"
+W = 4
+ROWS, COLS = 3072, 7168
+N = ROWS * COLS
+NB = N // 128
+M = N // W                 # values per ring chunk / A2A shard
+SETS = 3                   # rotating input sets (3 x 176 MB)
+
+# algorithmic bytes per 128 values of each kernel (inputs read once, outputs written once)
+B_QUANT = 256 + 132        # bf16 in; int8 + fp32 scale out
+B_DEQUANT = 132 + 256
+B_HOP = 132 + 256 + 132    # payload + local bf16 in; payload out
+B_ACCUM = lambda w: 132 * w + 256
+B_MX = 256 + 128 + 4       # bf16 in; E4M3 + 4 E8M0 bytes out (per 128 values)
+B_E4M3 = 256 + 132
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_wire_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Step:
+    """All buffers of one step and its launches as (name, algorithmic bytes, fn, args).
+
+    `calls` is the step as a user runs it: the two collective drivers, the MXFP8 slice
+    and dequantize calls and the E4M3 codec calls.  `kernels` is the same work as the
+    primitive calls the drivers make, one kernel launch each, for per-kernel timing.
+    """
+
+    def __init__(self, torch, bq, sets: int):
+        import workloads
+        self.torch, self.bq = torch, bq
+        L = self.L = bq.lib
+        dev = "cuda"
+        i16, i8, u8, f32 = torch.int16, torch.int8, torch.uint8, torch.float32
+        self.parts = []
+        for k in range(sets):
+            ranks = []
+            for r in range(W):
+                host = workloads.rows(2, r + 16 * k, 0, ROWS, COLS)
+                ranks.append(torch.from_numpy(host.view(np.int16)).to(dev))
+            self.parts.append(ranks)
+        e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
+        self.q_wire, self.s_wire = e(N, i8), e(NB, f32)
+        self.ring_out = [e(N, i16) for _ in range(W)]
+        self.q_send = [e(N, i8) for _ in range(W)]
+        self.s_send = [e(NB, f32) for _ in range(W)]
+        self.red, self.q_bc, self.s_bc = e(N, i16), e(N, i8), e(NB, f32)
+        self.a2a_out = [e(N, i16) for _ in range(W)]
+        self.mx_v = torch.empty((ROWS, W * COLS), dtype=u8, device=dev)
+        self.mx_e = torch.empty((ROWS, W * COLS // 32), dtype=u8, device=dev)
+        self.mx_y = torch.empty((ROWS, W * COLS), dtype=i16, device=dev)
+        self.e4_v, self.e4_s, self.e4_y = e(N, u8), e(NB, f32), e(N, i16)
+        self.stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        A = lambda ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
+        P = lambda t: t.data_ptr()
+        MB = M // 128
+        self.calls, self.kernels = [], []
+        for parts in self.parts:
+            calls, kern = [], []
+            xs = A([P(t) for t in parts])
+            # i8_ring driver; and its kernels: rank r starts with chunk r-1 and at step k
+            # folds chunk r-1-k into the payload it received
+            ring_bytes = NB * B_QUANT + (W - 1) * NB * B_HOP + W * NB * B_DEQUANT
+            calls.append(("i8_ring_allreduce", ring_bytes,
+                          L.bq_ring_allreduce_i8, (W, N, xs, P(self.q_wire), P(self.s_wire),
+                                                   A([P(t) for t in self.ring_out]), sp)))
+            chunk = lambda r, k: (r - 1 - k) % W
+            x0 = A([P(parts[r]) + 2 * M * chunk(r, 0) for r in range(W)])
+            q0 = A([P(self.q_wire) + M * chunk(r, 0) for r in range(W)])
+            s0 = A([P(self.s_wire) + 4 * MB * chunk(r, 0) for r in range(W)])
+            kern.append(("quant_i8 x4", NB * B_QUANT, L.bq_quant_i8_batch, (W, x0, M, q0, s0, sp)))
+            for k in range(1, W):
+                lk = A([P(parts[r]) + 2 * M * chunk(r, k) for r in range(W)])
+                qk = A([P(self.q_wire) + M * chunk(r, k) for r in range(W)])
+                sk = A([P(self.s_wire) + 4 * MB * chunk(r, k) for r in range(W)])
+                kern.append(("ring_hop_i8 x4", NB * B_HOP, L.bq_ring_hop_i8_batch,
+                             (W, qk, sk, lk, M, qk, sk, sp)))
+            kern.append(("dequant_i8 x4", W * NB * B_DEQUANT, L.bq_dequant_i8_batch,
+                         (W, A([P(self.q_wire)] * W), A([P(self.s_wire)] * W), N,
+                          A([P(t) for t in self.ring_out]), sp)))
+            # i8_a2a driver and its kernels
+            a2a_bytes = (W * NB * B_QUANT + W * MB * B_ACCUM(W) + NB * B_QUANT
+                         + W * NB * B_DEQUANT)
+            qsend, ssend = A([P(t) for t in self.q_send]), A([P(t) for t in self.s_send])
+            calls.append(("i8_a2a_allreduce", a2a_bytes,
+                          L.bq_a2a_allreduce_i8, (W, N, xs, qsend, ssend, P(self.red), P(self.q_bc),
+                                                  P(self.s_bc), A([P(t) for t in self.a2a_out]),
+                                                  sp)))
+            kern.append(("quant_i8 x4", W * NB * B_QUANT, L.bq_quant_i8_batch,
+                         (W, xs, N, qsend, ssend, sp)))
+            kern.append(("accum_i8 4src x4", W * MB * B_ACCUM(W), L.bq_dequant_accum_i8_batch,
+                         (W, W, qsend, ssend, M, P(self.red), sp)))
+            kern.append(("quant_i8 x1", NB * B_QUANT, L.bq_quant_i8_batch,
+                         (1, A([P(self.red)]), N, A([P(self.q_bc)]), A([P(self.s_bc)]), sp)))
+            kern.append(("dequant_i8 x4", W * NB * B_DEQUANT, L.bq_dequant_i8_batch,
+                         (W, A([P(self.q_bc)] * W), A([P(self.s_bc)] * W), N,
+                          A([P(t) for t in self.a2a_out]), sp)))
+            # MXFP8: the four partials as 128-aligned slices of the staging buffer
+            for r in range(W):
+                c = ("quant_mx_slice", NB * B_MX, L.bq_quant_mx_slice,
+                     (P(parts[r]), ROWS, COLS, COLS, COLS * r, P(self.mx_v), W * COLS,
+                      P(self.mx_e), W * COLS // 32, ROWS, sp))
+                calls.append(c)
+                kern.append(c)
+            c = ("dequant_mx", W * NB * B_MX, L.bq_dequant_mx,
+                 (P(self.mx_v), W * COLS, P(self.mx_e), W * COLS // 32, ROWS, W * COLS,
+                  P(self.mx_y), W * COLS, sp))
+            calls.append(c)
+            kern.append(c)
+            # E4M3 128-block codec on rank 0
+            for c in (("quant_e4m3_b128", NB * B_E4M3, L.bq_quant_e4m3_b128,
+                       (P(parts[0]), N, P(self.e4_v), P(self.e4_s), sp)),
+                      ("dequant_e4m3_b128", NB * B_E4M3, L.bq_dequant_e4m3_b128,
+                       (P(self.e4_v), P(self.e4_s), N, P(self.e4_y), sp))):
+                calls.append(c)
+                kern.append(c)
+            self.calls.append(calls)
+            self.kernels.append(kern)
+        assert sum(c[1] for c in self.calls[0]) == sum(k[1] for k in self.kernels[0])
+
+    @property
+    def step_bytes(self) -> int:
+        return sum(c[1] for c in self.calls[0])
+
+    def run(self, i: int) -> None:
+        for name, _, fn, args in self.calls[i % len(self.calls)]:
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st} ({self.bq.bq_status_str(st)})")
+
+    def run_kernels(self, i: int, events) -> None:
+        for k, (name, _, fn, args) in enumerate(self.kernels[i % len(self.kernels)]):
+            events[k][0].record(self.stream)
+            st = fn(*args)
+            events[k][1].record(self.stream)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st} ({self.bq.bq_status_str(st)})")
+
+
+def cpu_baseline(rows_per_rank: int) -> dict:
+    """The oracle, single-threaded, on the first `rows_per_rank` rows of every rank."""
+    import oracle
+    import workloads
+    R = rows_per_rank
+    parts = [workloads.rows(2, r, 0, R, COLS) for r in range(W)]
+    t0 = time.perf_counter()
+    oracle.ring_allreduce_i8([p.reshape(-1) for p in parts])
+    oracle.a2a_allreduce_i8([p.reshape(-1) for p in parts])
+    cat = np.concatenate(parts, axis=1)
+    v = np.empty((R, W * COLS), np.uint8)
+    e = np.empty((R, W * COLS // 32), np.uint8)
+    for r in range(W):
+        oracle.quant_mx_slice(parts[r], COLS * r, v, e)
+    oracle.dequant_mx(v, e)
+    ev, es = oracle.quant_e4m3_b128(parts[0])
+    oracle.dequant_e4m3_b128(ev, es)
+    dt = time.perf_counter() - t0
+    del cat
+    frac = R / ROWS
+    return {"seconds": dt, "frac": frac}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=96,
+                    help="rows per rank of the CPU-baseline sample (multiple of 4)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (a simulated rank is a separate HBM buffer on the one GPU)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30}))
+        return 0
+
+    import block_quantized_wire_amd as bq
+    step = Step(torch, bq, SETS)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: the whole step, eager launches, no per-kernel events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(step.stream)
+    for i in range(args.steps):
+        step.run(i)
+    t1.record(step.stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = step.step_bytes / (ms * 1e-3) / 1e9
+
+    # timed region 2: the same work as its primitive launches, HIP events around each
+    nl = len(step.kernels[0])
+    reps = max(1, args.steps // 4)
+    per = {}
+    for i in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(nl)]
+        step.run_kernels(i, ev)
+        torch.cuda.synchronize()
+        for k, (name, nbytes, _, _) in enumerate(step.kernels[i % len(step.kernels)]):
+            key = (name, nbytes)
+            d = per.setdefault(key, {"ms": []})
+            d["ms"].append(ev[k][0].elapsed_time(ev[k][1]))
+    kernels = {}
+    for (name, nbytes), d in per.items():
+        label = f"{name} ({nbytes} B)"
+        us = float(np.mean(d["ms"]) * 1e3)
+        kernels[label] = {"bytes_per_launch": nbytes, "launches_per_step": len(d["ms"]) // reps,
+                          "us_per_launch": us, "gbs": nbytes / (us * 1e-6) / 1e9}
+        kernels[label]["frac"] = kernels[label]["gbs"] / HBM_PEAK_GBS
+        kernels[label]["us_per_step"] = us * kernels[label]["launches_per_step"]
+    per = kernels
+    dom_name = max(per, key=lambda k: per[k]["us_per_step"])
+    dom = per[dom_name]
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("source_digest") == kernel_source_digest() and dom_name in t.get("kernels", {}):
+            traffic = t["kernels"][dom_name]
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "4 simulated ranks x 3072x7168 bf16 partials, N(0,0.5): i8_ring "
+                               "+ i8_a2a all-reduce, MXFP8 staged slices + dequant, E4M3-b128 codec",
+                   "ranks": W, "rows": ROWS, "cols": COLS, "input_sets": SETS,
+                   "step_bytes": step.step_bytes},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["gbs"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["frac"], 4),
+                     "bytes_per_launch": dom["bytes_per_launch"],
+                     "us_per_launch": round(dom["us_per_launch"], 2),
+                     "traffic": traffic},
+        "kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
+                        "launches_per_step": v["launches_per_step"],
+                        "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
+                        "frac": round(v["frac"], 4)} for k, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args.cpu_rows)
+        cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9
+        line["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"the same step on the first {args.cpu_rows} of "
+                                          f"{ROWS} rows of every rank ({cb['seconds']:.1f} s)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,270 @@
+"""libblockq: block-quantized wire codecs for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI declared in ``include/blockq.h``.  Every
+function here has the name of the C entry point it calls and only marshals
+arguments: torch tensors give device pointers, the stream defaults to torch's
+current stream, and a non-OK status raises :class:`BlockqError`.  All compute
+runs in the HIP kernels of ``libblockq.so``; there is no fallback, so importing
+fails loudly when the library has not been built.
+
+Tensor conventions: bf16 data as ``torch.bfloat16`` (or int16/uint16 bit
+views), INT8 payloads ``torch.int8``, E4M3 / E8M0 bytes ``torch.uint8``, block
+scales ``torch.float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BlockqError", "lib", "LIB_PATH",
+    "bq_quant_i8", "bq_dequant_i8", "bq_dequant_accum_i8", "bq_dequant_accum_i8_batch",
+    "bq_ring_hop_i8",
+    "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
+    "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
+    "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
+    "bq_quant_e4m3_b128", "bq_dequant_e4m3_b128",
+    "bq_wire_bytes_b128", "bq_status_str", "bq_version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libblockq.so")
+
+BQ_OK = 0
+BQ_STATUS = {0: "BQ_OK", 1: "BQ_ERR_NULL", 2: "BQ_ERR_SIZE", 3: "BQ_ERR_ALIGN",
+             4: "BQ_ERR_BOUNDS", 5: "BQ_ERR_NSRC", 6: "BQ_ERR_ALIAS", 7: "BQ_ERR_LAUNCH"}
+
+
+class BlockqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.name = BQ_STATUS.get(status, str(status))
+        super().__init__(f"{fn}: {self.name} ({_L().bq_status_str(status).decode()})")
+
+
+_P, _I, _I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_SIGS = {
+    "bq_quant_i8": [_P, _I64, _P, _P, _P],
+    "bq_dequant_i8": [_P, _P, _I64, _P, _P],
+    "bq_dequant_accum_i8": [_I, _PP, _PP, _I64, _P, _P],
+    "bq_dequant_accum_i8_batch": [_I, _I, _PP, _PP, _I64, _P, _P],
+    "bq_ring_hop_i8": [_P, _P, _P, _I64, _P, _P, _P],
+    "bq_quant_i8_batch": [_I, _PP, _I64, _PP, _PP, _P],
+    "bq_dequant_i8_batch": [_I, _PP, _PP, _I64, _PP, _P],
+    "bq_ring_hop_i8_batch": [_I, _PP, _PP, _PP, _I64, _PP, _PP, _P],
+    "bq_ring_allreduce_i8": [_I, _I64, _PP, _P, _P, _PP, _P],
+    "bq_a2a_allreduce_i8": [_I, _I64, _PP, _PP, _PP, _P, _P, _P, _PP, _P],
+    "bq_quant_mx": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
+    "bq_dequant_mx": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
+    "bq_quant_mx_slice": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
+    "bq_mx_staging_bytes": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "bq_quant_e4m3_b128": [_P, _I64, _P, _P, _P],
+    "bq_dequant_e4m3_b128": [_P, _P, _I64, _P, _P],
+}
+_lib = None
+
+
+def _L() -> ctypes.CDLL:
+    """The loaded libblockq.so (loaded on first use; a missing library is an error)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python block_quantized_wire_amd/build.py` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.bq_wire_bytes_b128.argtypes = [_I64]
+        L.bq_wire_bytes_b128.restype = _I64
+        L.bq_status_str.argtypes = [ctypes.c_int]
+        L.bq_status_str.restype = ctypes.c_char_p
+        L.bq_version.argtypes = []
+        L.bq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def __getattr__(name: str):
+    if name == "lib":
+        return _L()
+    raise AttributeError(name)
+
+
+# ---- marshalling helpers ---------------------------------------------------------------
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (or an int address, or None for NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptrs(ts) -> ctypes.Array:
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _numel(t) -> int:
+    return t.numel()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BQ_OK:
+        raise BlockqError(fn, status)
+
+
+# ---- block INT8 ----------------------------------------------------------------------------
+
+def bq_quant_i8(x, q, scale, n: int | None = None, stream=None) -> None:
+    n = _numel(x) if n is None else n
+    _check("bq_quant_i8", _L().bq_quant_i8(_ptr(x), n, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def bq_dequant_i8(q, scale, y, n: int | None = None, stream=None) -> None:
+    n = _numel(q) if n is None else n
+    _check("bq_dequant_i8", _L().bq_dequant_i8(_ptr(q), _ptr(scale), n, _ptr(y), _stream(stream)))
+
+
+def bq_dequant_accum_i8(q_srcs, s_srcs, y, n: int | None = None, stream=None) -> None:
+    n = _numel(y) if n is None else n
+    _check("bq_dequant_accum_i8",
+           _L().bq_dequant_accum_i8(len(q_srcs), _ptrs(q_srcs), _ptrs(s_srcs), n, _ptr(y),
+                                   _stream(stream)))
+
+
+def bq_dequant_accum_i8_batch(nseg: int, q_srcs, s_srcs, y, seg_n: int | None = None,
+                              stream=None) -> None:
+    seg_n = _numel(y) // nseg if seg_n is None else seg_n
+    _check("bq_dequant_accum_i8_batch",
+           _L().bq_dequant_accum_i8_batch(nseg, len(q_srcs), _ptrs(q_srcs), _ptrs(s_srcs), seg_n,
+                                         _ptr(y), _stream(stream)))
+
+
+def bq_ring_hop_i8(q_in, s_in, local, q_out, s_out, n: int | None = None, stream=None) -> None:
+    n = _numel(local) if n is None else n
+    _check("bq_ring_hop_i8", _L().bq_ring_hop_i8(_ptr(q_in), _ptr(s_in), _ptr(local), n,
+                                                _ptr(q_out), _ptr(s_out), _stream(stream)))
+
+
+def bq_quant_i8_batch(xs, qs, ss, n: int | None = None, stream=None) -> None:
+    n = _numel(xs[0]) if n is None else n
+    _check("bq_quant_i8_batch", _L().bq_quant_i8_batch(len(xs), _ptrs(xs), n, _ptrs(qs), _ptrs(ss),
+                                                      _stream(stream)))
+
+
+def bq_dequant_i8_batch(qs, ss, ys, n: int | None = None, stream=None) -> None:
+    n = _numel(ys[0]) if n is None else n
+    _check("bq_dequant_i8_batch", _L().bq_dequant_i8_batch(len(qs), _ptrs(qs), _ptrs(ss), n,
+                                                          _ptrs(ys), _stream(stream)))
+
+
+def bq_ring_hop_i8_batch(q_in, s_in, local, q_out, s_out, n: int | None = None,
+                         stream=None) -> None:
+    n = _numel(local[0]) if n is None else n
+    _check("bq_ring_hop_i8_batch",
+           _L().bq_ring_hop_i8_batch(len(q_in), _ptrs(q_in), _ptrs(s_in), _ptrs(local), n,
+                                    _ptrs(q_out), _ptrs(s_out), _stream(stream)))
+
+
+def bq_ring_allreduce_i8(partials, q_wire, s_wire, outs, n: int | None = None,
+                         stream=None) -> None:
+    n = _numel(partials[0]) if n is None else n
+    _check("bq_ring_allreduce_i8",
+           _L().bq_ring_allreduce_i8(len(partials), n, _ptrs(partials), _ptr(q_wire), _ptr(s_wire),
+                                    _ptrs(outs), _stream(stream)))
+
+
+def bq_a2a_allreduce_i8(partials, q_send, s_send, red, q_bcast, s_bcast, outs,
+                        n: int | None = None, stream=None) -> None:
+    n = _numel(partials[0]) if n is None else n
+    _check("bq_a2a_allreduce_i8",
+           _L().bq_a2a_allreduce_i8(len(partials), n, _ptrs(partials), _ptrs(q_send), _ptrs(s_send),
+                                   _ptr(red), _ptr(q_bcast), _ptr(s_bcast), _ptrs(outs),
+                                   _stream(stream)))
+
+
+# ---- MXFP8 -----------------------------------------------------------------------------------
+
+def bq_quant_mx(x, v, e8m0, rows: int | None = None, cols: int | None = None,
+                ldx: int | None = None, ldv: int | None = None, lds: int | None = None,
+                stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ldx = x.stride(0) if ldx is None else ldx
+    ldv = v.stride(0) if ldv is None else ldv
+    lds = e8m0.stride(0) if lds is None else lds
+    _check("bq_quant_mx", _L().bq_quant_mx(_ptr(x), rows, cols, ldx, _ptr(v), ldv, _ptr(e8m0), lds,
+                                          _stream(stream)))
+
+
+def bq_dequant_mx(v, e8m0, y, rows: int | None = None, cols: int | None = None,
+                  ldv: int | None = None, lds: int | None = None, ldy: int | None = None,
+                  stream=None) -> None:
+    rows = y.shape[0] if rows is None else rows
+    cols = y.shape[1] if cols is None else cols
+    ldv = v.stride(0) if ldv is None else ldv
+    lds = e8m0.stride(0) if lds is None else lds
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("bq_dequant_mx", _L().bq_dequant_mx(_ptr(v), ldv, _ptr(e8m0), lds, rows, cols, _ptr(y),
+                                              ldy, _stream(stream)))
+
+
+def bq_quant_mx_slice(x, col_off: int, v, e8m0, capacity_rows: int | None = None,
+                      rows: int | None = None, cols: int | None = None, ldx: int | None = None,
+                      ldv: int | None = None, lds: int | None = None, stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ldx = x.stride(0) if ldx is None else ldx
+    ldv = v.stride(0) if ldv is None else ldv
+    lds = e8m0.stride(0) if lds is None else lds
+    capacity_rows = v.shape[0] if capacity_rows is None else capacity_rows
+    _check("bq_quant_mx_slice",
+           _L().bq_quant_mx_slice(_ptr(x), rows, cols, ldx, col_off, _ptr(v), ldv, _ptr(e8m0), lds,
+                                 capacity_rows, _stream(stream)))
+
+
+def bq_mx_staging_bytes(capacity_rows: int, total_cols: int) -> tuple[int, int]:
+    vb, sb = ctypes.c_int64(), ctypes.c_int64()
+    _check("bq_mx_staging_bytes",
+           _L().bq_mx_staging_bytes(capacity_rows, total_cols, ctypes.byref(vb), ctypes.byref(sb)))
+    return vb.value, sb.value
+
+
+# ---- E4M3 128-block codec ------------------------------------------------------------------
+
+def bq_quant_e4m3_b128(x, v, scale, n: int | None = None, stream=None) -> None:
+    n = _numel(x) if n is None else n
+    _check("bq_quant_e4m3_b128", _L().bq_quant_e4m3_b128(_ptr(x), n, _ptr(v), _ptr(scale),
+                                                        _stream(stream)))
+
+
+def bq_dequant_e4m3_b128(v, scale, y, n: int | None = None, stream=None) -> None:
+    n = _numel(v) if n is None else n
+    _check("bq_dequant_e4m3_b128", _L().bq_dequant_e4m3_b128(_ptr(v), _ptr(scale), n, _ptr(y),
+                                                            _stream(stream)))
+
+
+# ---- host helpers --------------------------------------------------------------------------
+
+def bq_wire_bytes_b128(n: int) -> int:
+    return _L().bq_wire_bytes_b128(n)
+
+
+def bq_status_str(status: int) -> str:
+    return _L().bq_status_str(status).decode()
+
+
+def bq_version() -> str:
+    return _L().bq_version().decode()

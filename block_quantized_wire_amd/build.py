@@ -1,0 +1,61 @@
+"""Build libblockq.so (HIP for gfx950) in-tree with hipcc.
+
+Usage: python -m block_quantized_wire_amd.build   (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libblockq.so")
+SOURCES = ["bq_abi.cpp", "bq_i8.hip", "bq_mx.hip"]
+HEADERS = ["bq_device.h", "bq_launch.h"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # the codec definitions round every product and sum separately, in IEEE binary32
+    "-ffp-contract=off",
+    "-fno-fast-math",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    # keep the compiler from forming packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def sources() -> list[str]:
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 into block_quantized_wire_amd/libblockq.so."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [
+        os.path.join(ROOT, "include", "blockq.h")]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

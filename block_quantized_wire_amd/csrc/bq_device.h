@@ -1,0 +1,221 @@
+// bq_device.h -- device building blocks of the libblockq kernels (gfx950, wave64).
+//
+// Work layout shared by every kernel: a lane owns 8 consecutive values (one 16-byte
+// bf16 vector), 16 lanes (one DPP row) own one 128-value block, and a wave64 covers
+// a "tile" of 4 blocks = 512 values per step.  Per-block reductions therefore stay
+// inside one DPP row and never touch LDS.
+//
+// Arithmetic follows the codec definitions bit for bit (IEEE binary32, round to
+// nearest even, no contraction -- the library is compiled with -ffp-contract=off and
+// denormals enabled).  Two shortcuts are used where they are provably exact:
+//
+//  * Block scales.  fl32(a/127) == fl32(fl64(a) * fl64(1/127)) for every finite
+//    binary32 a: a/127 = M/127 * 2^k with M an integer, whose binary expansion is
+//    purely periodic with period 7 (2^7 = 1 mod 127) unless exact.  The part beyond
+//    the 24th significant bit is therefore p/127 of an ulp with p in 1..126, at least
+//    1/254 ulp away from the rounding midpoint (also in the subnormal range, where
+//    the grid is 2^-149), while the fp64 product is within 2^-52 relative.  The same
+//    argument with period 3 covers a/448 = (a/7) * 2^-6 for bf16 a (no exact
+//    midpoint is reachable from a bf16 numerator there either).
+//
+//  * Element quotients.  q0 = x * rcp(s) differs from x/s by at most
+//    |x/s| * 1.5 * 2^-23 (v_rcp_f32 is accurate to 1 ulp) and fl32(x/s) from x/s by
+//    |x/s| * 2^-24; with |x/s| <= 127.25 both stay below 2^-15.  Whenever q0 lies
+//    within 2^-13 of a half-integer (or is not finite), the exact IEEE division is
+//    done instead, so round-half-even(q0) == round-half-even(fl32(x/s)) always.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bq {
+
+constexpr int kBlock = 128;           // values per INT8 / E4M3 block
+constexpr int kLaneVals = 8;          // values per lane per tile
+constexpr int kTileBlocks = 4;        // blocks per wave64 tile
+constexpr int kTileVals = 512;        // values per wave64 tile
+constexpr int kWavesPerGroup = 4;     // 256-thread workgroups
+constexpr int kGroupThreads = 256;
+constexpr int kMaxBatch = 16;
+constexpr int kMaxSrc = 64;
+
+// ---- vector memory ----------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) 16- and 8-byte accesses: every byte is touched once.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st8(void* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+
+// ---- bf16 <-> binary32 --------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack_bf16x8(u32x4 w, float f[8]) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+    f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// Round two binary32 values to bf16 (nearest, ties to even; a carry out of the
+// significand moves into the exponent) and pack them, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7FFFu + ((ua >> 16) & 1u);
+    ub += 0x7FFFu + ((ub >> 16) & 1u);
+    return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float f[8]) {
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+}
+
+// ---- DPP row reductions (16 lanes) -----------------------------------------------------
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, false);
+}
+
+// Max of a non-negative binary32 (given as bits) over the 16 lanes of a DPP row.
+// For non-negative floats the integer order of the bit patterns is the float order.
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max(v, dpp<0x141>(v));   // row_half_mirror
+    v = max(v, dpp<0x140>(v));   // row_mirror
+    return v;
+}
+
+// Max over the 4 lanes of a quad (one MXFP8 group of 32 values).
+__device__ __forceinline__ uint32_t quad_max4(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));
+    v = max(v, dpp<0x4E>(v));
+    return v;
+}
+
+// ---- block INT8 ------------------------------------------------------------------------
+
+// fl32(amax / 127) without an fp32 division (exact; see the header comment).
+__device__ __forceinline__ float i8_scale(float amax) {
+    return (float)((double)amax * (1.0 / 127.0));
+}
+
+// fl32(amax / 448) for a bf16 amax (exact; see the header comment).
+__device__ __forceinline__ float e4m3_block_scale(float amax) {
+    return (float)((double)amax * (1.0 / 448.0));
+}
+
+// round-half-even(fl32(x / s)) for |x| <= amax, s = fl32(amax/127) > 0, r ~ 1/s.
+// Returns the integer as a float.  The result never exceeds 127 in magnitude:
+// amax / fl32(amax/127) <= 127 * (1 + 2^-9) even for subnormal scales, so the
+// clamp to [-127, 127] of the definition never changes a value.
+__device__ __forceinline__ float i8_round_quot(float x, float s, float r) {
+    float q0 = x * r;
+    float t = __builtin_rintf(q0);
+    float d = __builtin_fabsf(q0 - t);
+    if (!(d < 0.5f - 0x1.0p-13f))          // near a tie, or not finite: exact path
+        t = __builtin_rintf(x / s);
+    return t;
+}
+
+// Pack the low bytes of four int-valued floats (in [-127, 127]) into one word.
+__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
+    uint32_t ia = (uint32_t)(int)a, ib = (uint32_t)(int)b;
+    uint32_t ic = (uint32_t)(int)c, id = (uint32_t)(int)d;
+    uint32_t lo = __builtin_amdgcn_perm(ib, ia, 0x0C0C0400u);   // [a0, b0, 0, 0]
+    uint32_t hi = __builtin_amdgcn_perm(id, ic, 0x04000C0Cu);   // [0, 0, c0, d0]
+    return lo | hi;
+}
+
+// Quantize 8 binary32 values of one lane with its block's scale.  A block whose
+// amax is 0 -- or whose scale underflows to 0, which only binary32 sums can reach --
+// is a zero block: scale 0, payload 0.
+__device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
+    if (s == 0.0f)
+        return u32x2{};
+    float r = __builtin_amdgcn_rcpf(s);
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        t[i] = i8_round_quot(f[i], s, r);
+    return u32x2{pack_i8x4(t[0], t[1], t[2], t[3]), pack_i8x4(t[4], t[5], t[6], t[7])};
+}
+
+// Signed bytes of a word as binary32 (exact).
+__device__ __forceinline__ void unpack_i8x4(uint32_t w, float* f) {
+    f[0] = (float)(int)(int8_t)(w & 0xFF);
+    f[1] = (float)(int)(int8_t)((w >> 8) & 0xFF);
+    f[2] = (float)(int)(int8_t)((w >> 16) & 0xFF);
+    f[3] = (float)(int)(int8_t)(w >> 24);
+}
+
+__device__ __forceinline__ void unpack_i8x8(u32x2 w, float f[8]) {
+    unpack_i8x4(w.x, f);
+    unpack_i8x4(w.y, f + 4);
+}
+
+// ---- OCP E4M3FN ------------------------------------------------------------------------
+
+// E4M3FN encoding of a binary32, round to nearest even, magnitudes >= 448 saturate to
+// 448, sign kept (also of zero).  Written out in integer arithmetic on the bits.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {                 // >= 448
+        code = 0x7E;
+    } else if (a >= 0x3C800000u) {          // >= 2^-6: normal E4M3 range
+        // keep 3 mantissa bits, round half to even on the 20 dropped bits
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - ((127u - 7u) << 3);
+    } else {                                // subnormal E4M3: multiples of 2^-9
+        // adding 2^14 leaves a significand grid of 2^-9; RNE happens in the add
+        float t = __uint_as_float(a) + 16384.0f;
+        code = __float_as_uint(t) - 0x46800000u;
+    }
+    return sign | code;
+}
+
+// Exact binary32 value of an E4M3FN code (NaN codes are outside the contract).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    uint32_t ex = (c >> 3) & 0xFu, man = c & 7u;
+    float mag = (ex == 0) ? (float)man * 0x1.0p-9f
+                          : __uint_as_float(((ex + 120u) << 23) | (man << 20));
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// MXFP8 shared-scale byte from a bf16 amax given as its 15 magnitude bits: 127 for an
+// all-zero group; else 127 + (smallest e with 2^e >= fl32(amax/448)), clamped to
+// [-127, 127].  For amax = m * 2^k (m in [1, 2)) that e is k - 8 + [m > 1.75], i.e.
+// biased exponent - 8 plus one when the 7 stored significand bits exceed 96; bf16
+// subnormals and anything below clamp to byte 0.
+__device__ __forceinline__ uint32_t e8m0_from_bf16_amax(uint32_t h) {
+    if (h == 0)
+        return 127u;
+    int e = (int)(h >> 7) - 8 + (((h & 0x7Fu) > 96u) ? 1 : 0);
+    return (uint32_t)(e < 0 ? 0 : e);
+}
+
+// 2^(127 - byte) as binary32 for byte in [0, 254] (always a normal number here since
+// the quantizer never produces a byte above 247).
+__device__ __forceinline__ float e8m0_inv_scale(uint32_t byte) {
+    return __uint_as_float((254u - byte) << 23);
+}
+
+}  // namespace bq

@@ -1,0 +1,310 @@
+// bq_i8.hip -- block-INT8 wire codec kernels for gfx950.
+//
+// Definitions (pages: sparkinfer pull request #46, "feat(pcie_dma): add block-INT8 wire
+// modes for AG, ring, and A2A", sections Summary and Implementation):
+//   quantize      per 128-value block: scale = fl32(amax/127), q = rne(fl32(x/scale)) in
+//                 [-127, 127]; an all-zero block stores scale 0 and payload 0;
+//   materialize   y = bf16_rne(fl32(q * scale));
+//   accumulate    y = bf16_rne(sum over sources, in order, of fl32(q_s * scale_s)), summed
+//                 in binary32 starting from +0 (the all-to-all reduce);
+//   ring hop      requantize fl32(fl32(q * scale) + local) block by block (one fused
+//                 reduce-scatter hop; the binary32 sums are requantized directly).
+//
+// All kernels are HBM streaming kernels: 16-byte bf16 and 8-byte INT8 vectors per lane,
+// per-block amax through DPP row reductions (no LDS), no atomics, and a fixed order of
+// every floating-point operation, so results are deterministic and bit-reproducible.
+// Every kernel takes a batch of equal-size segments (grid.y = segment) so that one
+// launch covers all simulated ranks of a collective step.
+#include "bq_device.h"
+#include "bq_launch.h"
+
+namespace bq {
+
+namespace {
+
+struct QuantArgs {
+    const uint16_t* x[kMaxBatch];
+    int8_t* q[kMaxBatch];
+    float* s[kMaxBatch];
+    int64_t nb;   // blocks per segment
+};
+
+struct DequantArgs {
+    const int8_t* q[kMaxBatch];
+    const float* s[kMaxBatch];
+    uint16_t* y[kMaxBatch];
+    int64_t nb;
+};
+
+struct HopArgs {
+    const int8_t* q_in[kMaxBatch];
+    const float* s_in[kMaxBatch];
+    const uint16_t* local[kMaxBatch];
+    int8_t* q_out[kMaxBatch];
+    float* s_out[kMaxBatch];
+    int64_t nb;
+};
+
+struct AccumArgs {
+    const int8_t* q[kMaxSrc];
+    const float* s[kMaxSrc];
+    uint16_t* y;
+    int nsrc;
+    int64_t nb;       // blocks per segment
+    int64_t seg_n;    // values per segment (offset of segment j is j * seg_n)
+};
+
+// Tile bookkeeping common to all INT8 kernels: which block and which 8 values of it
+// this lane owns in tile u of its wave.
+struct LaneMap {
+    int64_t tile0;
+    int sub;      // block index within the tile (= DPP row of the lane)
+    int off;      // first value of the lane within its block
+    bool leader;  // first lane of the row: stores the block's scale
+    __device__ LaneMap(int U) {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        sub = lane >> 4;
+        off = (lane & 15) * kLaneVals;
+        leader = (lane & 15) == 0;
+    }
+    __device__ int64_t block(int u) const { return (tile0 + u) * kTileBlocks + sub; }
+};
+
+template <int U>
+__global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
+    const uint16_t* __restrict__ x = a.x[blockIdx.y];
+    int8_t* __restrict__ q = a.q[blockIdx.y];
+    float* __restrict__ s = a.s[blockIdx.y];
+    const LaneMap L(U);
+    u32x4 xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        xv[u] = (b < a.nb) ? ld16(x + b * kBlock + L.off) : u32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        float f[8];
+        unpack_bf16x8(xv[u], f);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+        const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+        const float sc = i8_scale(amax);
+        const u32x2 qv = quant_i8x8(f, sc);
+        if (b < a.nb) {
+            st8(q + b * kBlock + L.off, qv);
+            if (L.leader)
+                s[b] = sc;
+        }
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(kGroupThreads) void k_dequant_i8(DequantArgs a) {
+    const int8_t* __restrict__ q = a.q[blockIdx.y];
+    const float* __restrict__ s = a.s[blockIdx.y];
+    uint16_t* __restrict__ y = a.y[blockIdx.y];
+    const LaneMap L(U);
+    u32x2 qv[U];
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        const bool in = b < a.nb;
+        qv[u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
+        sv[u] = in ? s[b] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        float f[8];
+        unpack_i8x8(qv[u], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            f[i] = f[i] * sv[u];
+        if (b < a.nb)
+            st16(y + b * kBlock + L.off, pack_bf16x8(f));
+    }
+}
+
+// q_in/q_out and s_in/s_out may be the same buffers: every lane loads its whole share
+// of a block before the block's stores, and no other wave touches that block.
+template <int U>
+__global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
+    const int8_t* q_in = a.q_in[blockIdx.y];
+    const float* s_in = a.s_in[blockIdx.y];
+    const uint16_t* __restrict__ local = a.local[blockIdx.y];
+    int8_t* q_out = a.q_out[blockIdx.y];
+    float* s_out = a.s_out[blockIdx.y];
+    const LaneMap L(U);
+    u32x2 qv[U];
+    u32x4 lv[U];
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        const bool in = b < a.nb;
+        qv[u] = in ? ld8(q_in + b * kBlock + L.off) : u32x2{};
+        sv[u] = in ? s_in[b] : 0.0f;
+        lv[u] = in ? ld16(local + b * kBlock + L.off) : u32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        float deq[8], loc[8], sum[8];
+        unpack_i8x8(qv[u], deq);
+        unpack_bf16x8(lv[u], loc);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            deq[i] = deq[i] * sv[u];        // rounded product ...
+            sum[i] = deq[i] + loc[i];       // ... then a rounded add (no contraction)
+            m = __builtin_fmaxf(m, __builtin_fabsf(sum[i]));
+        }
+        const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+        const float sc = i8_scale(amax);
+        const u32x2 out = quant_i8x8(sum, sc);
+        if (b < a.nb) {
+            st8(q_out + b * kBlock + L.off, out);
+            if (L.leader)
+                s_out[b] = sc;
+        }
+    }
+}
+
+// Sources are consumed in chunks of 8 whose loads are all issued before the chunk's
+// ordered additions, so up to 8 independent 8-byte streams are in flight per lane.
+template <int U>
+__global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
+    const int64_t seg_off = (int64_t)blockIdx.y * a.seg_n;
+    const int64_t seg_sb = seg_off / kBlock;
+    uint16_t* __restrict__ y = a.y + seg_off;
+    const LaneMap L(U);
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[u][i] = 0.0f;
+    for (int k0 = 0; k0 < a.nsrc; k0 += 8) {
+        u32x2 qv[8][U];
+        float sv[8][U];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (k0 + j < a.nsrc) {
+                const int8_t* q = a.q[k0 + j] + seg_off;
+                const float* s = a.s[k0 + j] + seg_sb;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t b = L.block(u);
+                    const bool in = b < a.nb;
+                    qv[j][u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
+                    sv[j][u] = in ? s[b] : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (k0 + j < a.nsrc) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float f[8];
+                    unpack_i8x8(qv[j][u], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float term = f[i] * sv[j][u];
+                        acc[u][i] = acc[u][i] + term;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = L.block(u);
+        if (b < a.nb)
+            st16(y + b * kBlock + L.off, pack_bf16x8(acc[u]));
+    }
+}
+
+// Launch shape: 256-thread workgroups of 4 waves, each wave U tiles of 4 blocks.
+template <int U>
+dim3 grid_for(int64_t nb, int count) {
+    const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
+    return dim3((unsigned)((nb + per_group - 1) / per_group), (unsigned)count, 1);
+}
+
+constexpr int kUQuant = 4;
+constexpr int kUDequant = 4;
+constexpr int kUHop = 2;
+constexpr int kUAccum = 1;
+
+}  // namespace
+
+hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
+                           float* const* s, int64_t n, hipStream_t stream) {
+    QuantArgs a{};
+    for (int i = 0; i < count; ++i) {
+        a.x[i] = x[i];
+        a.q[i] = q[i];
+        a.s[i] = s[i];
+    }
+    a.nb = n / kBlock;
+    hipLaunchKernelGGL(k_quant_i8<kUQuant>, grid_for<kUQuant>(a.nb, count), dim3(kGroupThreads),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
+                             uint16_t* const* y, int64_t n, hipStream_t stream) {
+    DequantArgs a{};
+    for (int i = 0; i < count; ++i) {
+        a.q[i] = q[i];
+        a.s[i] = s[i];
+        a.y[i] = y[i];
+    }
+    a.nb = n / kBlock;
+    hipLaunchKernelGGL(k_dequant_i8<kUDequant>, grid_for<kUDequant>(a.nb, count),
+                       dim3(kGroupThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
+                              const uint16_t* const* local, int8_t* const* q_out,
+                              float* const* s_out, int64_t n, hipStream_t stream) {
+    HopArgs a{};
+    for (int i = 0; i < count; ++i) {
+        a.q_in[i] = q_in[i];
+        a.s_in[i] = s_in[i];
+        a.local[i] = local[i];
+        a.q_out[i] = q_out[i];
+        a.s_out[i] = s_out[i];
+    }
+    a.nb = n / kBlock;
+    hipLaunchKernelGGL(k_ring_hop_i8<kUHop>, grid_for<kUHop>(a.nb, count), dim3(kGroupThreads),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
+                           uint16_t* y, int nseg, int64_t seg_n, hipStream_t stream) {
+    AccumArgs a{};
+    for (int i = 0; i < nsrc; ++i) {
+        a.q[i] = q[i];
+        a.s[i] = s[i];
+    }
+    a.y = y;
+    a.nsrc = nsrc;
+    a.nb = seg_n / kBlock;
+    a.seg_n = seg_n;
+    hipLaunchKernelGGL(k_accum_i8<kUAccum>, grid_for<kUAccum>(a.nb, nseg), dim3(kGroupThreads),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace bq

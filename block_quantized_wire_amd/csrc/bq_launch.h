@@ -1,0 +1,40 @@
+// bq_launch.h -- internal launchers of the libblockq kernels (host side).
+//
+// Arguments are assumed valid: the public entry points in bq_abi.cpp validate every
+// pointer, size, alignment and overlap before calling these.  Each launcher enqueues
+// one kernel on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bq {
+
+// Block INT8.  Segment i of a batch is (x[i] -> q[i], s[i]), n values each.
+hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
+                           float* const* s, int64_t n, hipStream_t stream);
+hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
+                             uint16_t* const* y, int64_t n, hipStream_t stream);
+hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
+                              const uint16_t* const* local, int8_t* const* q_out,
+                              float* const* s_out, int64_t n, hipStream_t stream);
+// nseg segments of seg_n values: segment j reads q[k] + j*seg_n (scales likewise) for
+// every source k in order and writes y + j*seg_n.
+hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
+                           uint16_t* y, int nseg, int64_t seg_n, hipStream_t stream);
+
+// MXFP8 (row-major with leading dimensions; cols a multiple of 128).
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds,
+                           hipStream_t stream);
+hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
+                             int64_t rows, int64_t cols, uint16_t* y, int64_t ldy,
+                             hipStream_t stream);
+
+// E4M3 128-block codec.
+hipError_t launch_quant_e4m3_b128(const uint16_t* x, uint8_t* v, float* s, int64_t n,
+                                  hipStream_t stream);
+hipError_t launch_dequant_e4m3_b128(const uint8_t* v, const float* s, uint16_t* y, int64_t n,
+                                    hipStream_t stream);
+
+}  // namespace bq

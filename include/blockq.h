@@ -1,0 +1,205 @@
+/*
+ * blockq.h -- C ABI of libblockq, block-quantized wire codecs for AMD MI355X (gfx950).
+ *
+ * Pages cited:
+ *   P1 = sparkinfer pull request #46, "feat(pcie_dma): add block-INT8 wire modes for AG,
+ *        ring, and A2A" (sections Summary, Implementation, Evidence).
+ *   P2 = sparkinfer pull request #72, "feat(pcie_dma): add INT8 and MXFP8 wire modes"
+ *        (PR body Summary / Modes / Configuration; review comment showing mxfp8_scale_byte).
+ *   P4 = b12x pull request #241, "[II] Support staged MXFP8 linear inputs" (sections
+ *        Behavior, Compatibility, Validation).
+ *
+ * Conventions (every entry point):
+ *   - Pointers named in a signature are DEVICE pointers unless marked "host array";
+ *     a host array is a host-memory array of device pointers, read during the call only.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  INT8 payloads are int8_t, E4M3
+ *     and E8M0 bytes are uint8_t, per-block scales are float (IEEE binary32).
+ *   - n counts values; it must be a multiple of 128 (a block, P1 Summary; the per-rank
+ *     shard rule of P2 Configuration).  n == 0 is valid and launches nothing.
+ *   - Layout of an INT8 or E4M3 block payload is planar: n payload bytes, and nb = n/128
+ *     scales in a separate array.  Together they are 132 bytes per 128 values (P1
+ *     Summary); a caller may place the scale array right after the payload in one
+ *     wire buffer.
+ *   - Ownership: the caller allocates and owns every buffer.  The library never
+ *     allocates, frees or synchronizes, holds no state between calls and is reentrant.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call enqueues its kernels and returns; inputs must stay unchanged until the stream
+ *     reaches the work.  No call synchronizes, so calls may be captured in a HIP graph.
+ *   - Errors: every argument is validated on the host before anything is launched; on
+ *     an error the call returns a status, writes nothing and launches nothing.
+ *     BQ_ERR_LAUNCH reports a failure of the launch itself (hipGetLastError).
+ *   - Alignment: bf16 and payload pointers 16-byte aligned; float scale arrays 4-byte
+ *     aligned; E8M0 scale arrays 4-byte aligned with a row stride divisible by 4.
+ *   - Aliasing: outputs must not overlap inputs or each other, except where an entry
+ *     point states an exact in-place form.  Partial overlap is BQ_ERR_ALIAS.
+ *   - Arithmetic: IEEE binary32 with round-to-nearest-even; no fused multiply-add where
+ *     the definitions below round a product; denormals are honoured.  Non-finite inputs
+ *     are outside the contract.
+ */
+#ifndef BLOCKQ_H
+#define BLOCKQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bq_status {
+    BQ_OK = 0,
+    BQ_ERR_NULL = 1,    /* a required pointer is NULL */
+    BQ_ERR_SIZE = 2,    /* a count or shape is negative or not a multiple of its block */
+    BQ_ERR_ALIGN = 3,   /* a pointer or leading dimension breaks the alignment rules */
+    BQ_ERR_BOUNDS = 4,  /* a leading dimension, offset or capacity does not fit */
+    BQ_ERR_NSRC = 5,    /* a source / rank / segment count is outside its range */
+    BQ_ERR_ALIAS = 6,   /* an output overlaps an input or another output */
+    BQ_ERR_LAUNCH = 7   /* the HIP launch failed */
+} bq_status;
+
+#define BQ_BLOCK 128        /* values per INT8 / E4M3 block */
+#define BQ_MX_GROUP 32      /* values per MXFP8 scale group */
+#define BQ_MAX_SRC 64       /* most sources of bq_dequant_accum_i8 */
+#define BQ_MAX_BATCH 16     /* most segments of a batched call; most simulated ranks */
+
+/* ==== Block-INT8 codec (P1 Summary, Implementation) ================================ */
+
+/* BF16 -> signed INT8, one FP32 scale per 128 values.  For each block of 128 consecutive
+ * values: amax = max |x|; scale = amax / 127 (binary32 division); q = round-half-even
+ * (x / scale) clamped to [-127, 127].  An all-zero block stores scale +0 and payload 0.
+ * x: bf16[n]; q: int8[n]; scale: float[n/128]. */
+bq_status bq_quant_i8(const uint16_t* x, int64_t n, int8_t* q, float* scale, void* stream);
+
+/* INT8 -> BF16 materialization: y = bf16_rne(fl32((float)q * scale)).
+ * q: int8[n]; scale: float[n/128]; y: bf16[n]. */
+bq_status bq_dequant_i8(const int8_t* q, const float* scale, int64_t n, uint16_t* y,
+                        void* stream);
+
+/* Multi-source INT8 dequantize with FP32 accumulation (the all-to-all reduce).
+ * For each value: acc = +0; for s = 0 .. nsrc-1 in that order: acc = acc + fl32(q_s *
+ * scale_s) (the product is rounded before the add); y = bf16_rne(acc).
+ * q_srcs, s_srcs: host arrays of nsrc device pointers (int8[n], float[n/128]);
+ * 1 <= nsrc <= BQ_MAX_SRC, else BQ_ERR_NSRC.  y: bf16[n]. */
+bq_status bq_dequant_accum_i8(int nsrc, const int8_t* const* q_srcs, const float* const* s_srcs,
+                              int64_t n, uint16_t* y, void* stream);
+
+/* Batched form of the accumulate: `nseg` owners (1..BQ_MAX_BATCH) in one launch.  Owner j
+ * sums shard j of every source: values [j*seg_n, (j+1)*seg_n) of q_srcs[k] (scales
+ * likewise), k = 0 .. nsrc-1 in that order, into y + j*seg_n.  Each source holds
+ * nseg*seg_n values; y holds nseg*seg_n values; seg_n a multiple of 128. */
+bq_status bq_dequant_accum_i8_batch(int nseg, int nsrc, const int8_t* const* q_srcs,
+                                    const float* const* s_srcs, int64_t seg_n, uint16_t* y,
+                                    void* stream);
+
+/* One fused ring reduce-scatter hop: per value sum = fl32(fl32(q_in * s_in) + local) in
+ * binary32, then the binary32 sums of each block are requantized with the
+ * bq_quant_i8 rule (no bf16 intermediate).  q_in: int8[n]; s_in: float[n/128];
+ * local: bf16[n]; q_out: int8[n]; s_out: float[n/128].  In place is allowed when
+ * q_out == q_in AND s_out == s_in exactly; any other overlap is BQ_ERR_ALIAS. */
+bq_status bq_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* local,
+                         int64_t n, int8_t* q_out, float* s_out, void* stream);
+
+/* Batched forms: `count` (1..BQ_MAX_BATCH) independent segments of n values each, one
+ * launch -- the simulated ranks of one collective step.  Each array argument is a host
+ * array of `count` device pointers; segment i is exactly the single call on element i.
+ * The in-place rule of bq_ring_hop_i8 applies per segment; segments must not overlap
+ * each other's outputs. */
+bq_status bq_quant_i8_batch(int count, const uint16_t* const* x, int64_t n, int8_t* const* q,
+                            float* const* scale, void* stream);
+bq_status bq_dequant_i8_batch(int count, const int8_t* const* q, const float* const* scale,
+                              int64_t n, uint16_t* const* y, void* stream);
+bq_status bq_ring_hop_i8_batch(int count, const int8_t* const* q_in, const float* const* s_in,
+                               const uint16_t* const* local, int64_t n, int8_t* const* q_out,
+                               float* const* s_out, void* stream);
+
+/* ==== Collectives simulated on one GPU: a "rank" is a separate HBM buffer ========== */
+
+/* i8_ring all-reduce (P1 Summary): INT8 ring reduce-scatter, then INT8 all-gather of
+ * the final payloads.  The n values of every rank are cut into `world` equal chunks
+ * (n divisible by 128*world), chunk c owned by rank c.  Step 0: rank r quantizes its
+ * chunk (r-1) mod W; steps k = 1..W-1: rank r folds its chunk (r-1-k) mod W into the
+ * payload it received with one fused hop; every rank, owner included, then
+ * materializes every chunk from that same final payload (the rank-consistency rule
+ * of P1 Summary).  One launch per step covers all ranks.
+ * partials: host array of W device pointers, bf16[n] each (read only);
+ * q_wire: int8[n], s_wire: float[n/128] -- caller-owned wire buffers; on return (in
+ * stream order) they hold the final payload of every chunk, chunk c at offset c*n/W;
+ * out: host array of W device pointers, bf16[n] each.  1 <= W <= BQ_MAX_BATCH. */
+bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                               int8_t* q_wire, float* s_wire, uint16_t* const* out,
+                               void* stream);
+
+/* i8_a2a all-reduce (P1 Summary, Implementation): every rank quantizes its partial
+ * once into q_send[r]/s_send[r]; owner j dequantizes shard j of the W payloads and
+ * accumulates them in binary32 in rank order into red (bf16, shard j at offset j*n/W);
+ * it requantizes that bf16 sum once into q_bcast/s_bcast; every rank materializes
+ * every shard from that broadcast payload into out[r].
+ * partials, q_send, s_send, out: host arrays of W device pointers (bf16[n], int8[n],
+ * float[n/128], bf16[n]); red: bf16[n]; q_bcast: int8[n]; s_bcast: float[n/128].
+ * n divisible by 128*world; 1 <= W <= BQ_MAX_BATCH. */
+bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                              int8_t* const* q_send, float* const* s_send, uint16_t* red,
+                              int8_t* q_bcast, float* s_bcast, uint16_t* const* out,
+                              void* stream);
+
+/* ==== MXFP8 (P2 Summary; review comment showing mxfp8_scale_byte; P4 Behavior) ===== */
+
+/* BF16 rows -> E4M3 values with one E8M0 scale per 32 consecutive columns of a row.
+ * Scale byte of a group: 127 if amax == 0, else 127 + the smallest e with
+ * 2^e >= fl32(amax / 448), clamped to [-127, 127].  Values: v = e4m3_rne_sat(x * 2^-(byte-127)),
+ * OCP E4M3FN, round-half-even, saturating at +-448, sign of zero kept.
+ * x: bf16[rows][ldx]; v: u8[rows][ldv]; e8m0: u8[rows][lds], scale (r, g) covers
+ * columns [32g, 32g+32).  cols a multiple of 128; ldx >= cols, ldx % 8 == 0;
+ * ldv >= cols, ldv % 16 == 0; lds >= cols/32, lds % 4 == 0. */
+bq_status bq_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* v,
+                      int64_t ldv, uint8_t* e8m0, int64_t lds, void* stream);
+
+/* MXFP8 -> BF16: y = bf16_rne(fl32(e4m3 * 2^(byte-127))).  Same layout rules; y is
+ * bf16[rows][ldy], ldy >= cols, ldy % 8 == 0. */
+bq_status bq_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
+                        int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, void* stream);
+
+/* Staged slice quantization (P4 Behavior, Compatibility): one BF16 slice of rows x cols
+ * is quantized with the bq_quant_mx rule into columns [col_off, col_off+cols) of the
+ * caller-owned staging buffer v (row stride ldv = total columns) and into scale
+ * columns [col_off/32, (col_off+cols)/32) of e8m0 (row stride lds).  cols and col_off
+ * must be multiples of 128; col_off + cols <= ldv; lds >= ldv/32; rows <=
+ * capacity_rows (the staging buffer's row capacity).  Rows at or above `rows` and
+ * columns outside the slice are not touched. */
+bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                            int64_t lds, int64_t capacity_rows, void* stream);
+
+/* Sizes of a staging buffer for `capacity_rows` rows of `total_cols` columns (the
+ * allocation helper of P4 Behavior, as a host-side size query: the caller allocates).
+ * total_cols must be a multiple of 128.  Host pointers. */
+bq_status bq_mx_staging_bytes(int64_t capacity_rows, int64_t total_cols, int64_t* value_bytes,
+                              int64_t* scale_bytes);
+
+/* ==== E4M3 128-block codec: the format the INT8 codec replaces (P1 Summary, Why) ==== */
+
+/* Same block and footprint as the INT8 codec (132 bytes per 128 values): scale =
+ * fl32(amax / 448); v = e4m3_rne_sat(fl32(x / scale)); an all-zero block stores scale
+ * +0 and every byte 0x00.  x: bf16[n]; v: u8[n]; scale: float[n/128]. */
+bq_status bq_quant_e4m3_b128(const uint16_t* x, int64_t n, uint8_t* v, float* scale,
+                             void* stream);
+
+/* y = bf16_rne(fl32(e4m3(v) * scale)).  v: u8[n]; scale: float[n/128]; y: bf16[n]. */
+bq_status bq_dequant_e4m3_b128(const uint8_t* v, const float* scale, int64_t n, uint16_t* y,
+                               void* stream);
+
+/* ==== Host helpers ================================================================ */
+
+/* Wire/staging bytes of n values in any 128-value block format: 132 * n / 128
+ * (P1 Summary; P2 Summary).  Returns -1 if n is negative or not a multiple of 128. */
+int64_t bq_wire_bytes_b128(int64_t n);
+
+/* Static description of a status code. */
+const char* bq_status_str(bq_status status);
+
+/* Library version string. */
+const char* bq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLOCKQ_H */

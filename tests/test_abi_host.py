@@ -1,0 +1,179 @@
+"""The C ABI on the host: the library loads, exports every declared entry point, and
+rejects every invalid argument with its status code before anything is launched.
+
+No call here reaches a kernel launch: every case fails validation, so the tests run
+without a GPU.  The addresses used are never dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+from block_quantized_wire_amd import build as _build  # noqa: E402
+
+if _build.stale():
+    _build.build()
+
+import block_quantized_wire_amd as bq  # noqa: E402
+
+L = bq.lib
+OK, NULL, SIZE, ALIGN, BOUNDS, NSRC, ALIAS = range(7)
+A = 1 << 32          # a 16-byte aligned fake device address
+S = 0                # default stream
+
+
+def arr(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "blockq.h")).read()
+    return sorted(set(re.findall(r"\b(bq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_symbols()
+    assert len(names) >= 18
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_host_helpers():
+    assert L.bq_wire_bytes_b128(128) == 132
+    assert L.bq_wire_bytes_b128(512 * 7168) == 132 * 512 * 56
+    assert L.bq_wire_bytes_b128(0) == 0
+    assert L.bq_wire_bytes_b128(100) == -1 and L.bq_wire_bytes_b128(-128) == -1
+    assert bq.bq_mx_staging_bytes(4096, 43008) == (4096 * 43008, 4096 * 1344)
+    with pytest.raises(bq.BlockqError) as e:
+        bq.bq_mx_staging_bytes(4096, 100)
+    assert e.value.status == SIZE
+    assert bq.bq_status_str(0) == "ok"
+    assert "alias" in bq.bq_status_str(6) or "overlap" in bq.bq_status_str(6)
+    assert "gfx950" in bq.bq_version()
+
+
+def test_quant_i8_errors():
+    n = 1024
+    assert L.bq_quant_i8(A, 100, A + 8192, A + 16384, S) == SIZE
+    assert L.bq_quant_i8(A, -128, A + 8192, A + 16384, S) == SIZE
+    assert L.bq_quant_i8(A, 0, A + 8192, A + 16384, S) == OK          # empty: nothing to do
+    assert L.bq_quant_i8(None, n, A + 8192, A + 16384, S) == NULL
+    assert L.bq_quant_i8(A, n, None, A + 16384, S) == NULL
+    assert L.bq_quant_i8(A + 8, n, A + 8192, A + 16384, S) == ALIGN
+    assert L.bq_quant_i8(A, n, A + 8200, A + 16384, S) == ALIGN
+    assert L.bq_quant_i8(A, n, A + 8192, A + 16386, S) == ALIGN
+    assert L.bq_quant_i8(A, n, A + 1024, A + 16384, S) == ALIAS      # q inside x
+    assert L.bq_quant_i8(A, n, A + 8192, A + 8192 + 512, S) == ALIAS  # scales inside q
+
+
+def test_dequant_and_e4m3_errors():
+    n = 1024
+    assert L.bq_dequant_i8(A, A + 4096, 130, A + 8192, S) == SIZE
+    assert L.bq_dequant_i8(A, None, n, A + 8192, S) == NULL
+    assert L.bq_dequant_i8(A, A + 4096, n, A + 4, S) == ALIGN
+    assert L.bq_dequant_i8(A, A + 4096, n, A + 512, S) == ALIAS
+    assert L.bq_quant_e4m3_b128(A, n, A + 1024, A + 8192, S) == ALIAS
+    assert L.bq_quant_e4m3_b128(A, n, None, A + 8192, S) == NULL
+    assert L.bq_dequant_e4m3_b128(A, A + 4096, n, A + 4096 + 16, S) == ALIAS
+    assert L.bq_dequant_e4m3_b128(A, A + 4096, 7, A + 8192, S) == SIZE
+
+
+def test_batch_counts_and_cross_segment_overlap():
+    n = 1024
+    x = arr(A, A + 4096)
+    q = arr(A + 8192, A + 8192 + 1024)
+    s = arr(A + 16384, A + 16384 + 64)
+    assert L.bq_quant_i8_batch(0, x, n, q, s, S) == NSRC
+    assert L.bq_quant_i8_batch(17, x, n, q, s, S) == NSRC
+    q_bad = arr(A + 8192, A + 8192 + 512)          # second segment's q overlaps the first's
+    assert L.bq_quant_i8_batch(2, x, n, q_bad, s, S) == ALIAS
+    y = arr(A + 32768, A + 32768 + 1024)            # outputs overlap each other
+    assert L.bq_dequant_i8_batch(2, q, s, n, y, S) == ALIAS
+
+
+def test_ring_hop_in_place_rules():
+    n = 1024
+    qi, si, loc = A, A + 4096, A + 8192
+    # partial overlap of q_out with q_in
+    assert L.bq_ring_hop_i8(qi, si, loc, n, qi + 16, si, S) == ALIAS
+    # q in place but scales not in place (and not disjoint either)
+    assert L.bq_ring_hop_i8(qi, si, loc, n, qi, si + 4, S) == ALIAS
+    # q in place, scales to a disjoint buffer: not an exact in-place pair
+    assert L.bq_ring_hop_i8(qi, si, loc, n, qi, A + 65536, S) == ALIAS
+    # output over the local partial
+    assert L.bq_ring_hop_i8(qi, si, loc, n, loc + 16, A + 65536, S) == ALIAS
+    assert L.bq_ring_hop_i8(qi, si, None, n, A + 65536, A + 70000, S) == NULL
+    assert L.bq_ring_hop_i8(qi, si, loc, n, A + 65536 + 8, A + 70000, S) == ALIGN
+    assert L.bq_ring_hop_i8(qi, si, loc, 1000, A + 65536, A + 70000, S) == SIZE
+
+
+def test_accum_errors():
+    n = 1024
+    qs = arr(A, A + 4096)
+    ss = arr(A + 8192, A + 8192 + 64)
+    assert L.bq_dequant_accum_i8(0, qs, ss, n, A + 65536, S) == NSRC
+    big = arr(*([A] * 65))
+    assert L.bq_dequant_accum_i8(65, big, big, n, A + 65536, S) == NSRC
+    assert L.bq_dequant_accum_i8(2, qs, ss, n, A + 4096 - 16, S) == ALIAS
+    assert L.bq_dequant_accum_i8(2, qs, ss, n, None, S) == NULL
+    assert L.bq_dequant_accum_i8(2, None, ss, n, A + 65536, S) == NULL
+    f = L.bq_dequant_accum_i8_batch
+    assert f(0, 2, qs, ss, n, A + 65536, S) == NSRC
+    assert f(17, 2, qs, ss, n, A + 65536, S) == NSRC
+    assert f(2, 0, qs, ss, n, A + 65536, S) == NSRC
+    assert f(2, 2, qs, ss, 100, A + 65536, S) == SIZE
+    assert f(4, 2, qs, ss, n, A + 2048, S) == ALIAS       # y over the sources' 4*n values
+
+
+def test_collective_driver_errors():
+    n = 4 * 1024
+    parts = arr(A, A + 16384, A + 32768, A + 49152)
+    outs = arr(A + 2 ** 20, A + 2 ** 20 + 16384, A + 2 ** 20 + 32768, A + 2 ** 20 + 49152)
+    qw, sw = A + 2 ** 21, A + 2 ** 21 + 8192
+    assert L.bq_ring_allreduce_i8(0, n, parts, qw, sw, outs, S) == NSRC
+    assert L.bq_ring_allreduce_i8(17, n, parts, qw, sw, outs, S) == NSRC
+    assert L.bq_ring_allreduce_i8(4, 128 * 6, parts, qw, sw, outs, S) == SIZE   # not 128*W
+    bad_outs = arr(A + 2 ** 20, A + 2 ** 20 + 16384, A + 2 ** 20 + 32768, A + 100 * 16)
+    assert L.bq_ring_allreduce_i8(4, n, parts, qw, sw, bad_outs, S) == ALIAS
+    assert L.bq_ring_allreduce_i8(4, n, parts, qw, qw + 1024, outs, S) == ALIAS  # wire overlap
+    assert L.bq_ring_allreduce_i8(4, n, parts, None, sw, outs, S) == NULL
+    qsend = arr(A + 2 ** 22, A + 2 ** 22 + 8192, A + 2 ** 22 + 16384, A + 2 ** 22 + 24576)
+    ssend = arr(A + 2 ** 23, A + 2 ** 23 + 256, A + 2 ** 23 + 512, A + 2 ** 23 + 768)
+    red, qb, sb = A + 2 ** 24, A + 2 ** 24 + 16384, A + 2 ** 24 + 32768
+    assert L.bq_a2a_allreduce_i8(4, n, parts, qsend, ssend, A, qb, sb, outs, S) == ALIAS
+    assert L.bq_a2a_allreduce_i8(4, 128 * 2, parts, qsend, ssend, red, qb, sb, outs, S) == SIZE
+    assert L.bq_a2a_allreduce_i8(0, n, parts, qsend, ssend, red, qb, sb, outs, S) == NSRC
+
+
+def test_mx_errors():
+    rows, cols = 16, 512
+    x, v, e = A, A + 2 ** 20, A + 2 ** 21
+    assert L.bq_quant_mx(x, rows, 100, 512, v, 512, e, 16, S) == SIZE
+    assert L.bq_quant_mx(x, rows, cols, 256, v, 512, e, 16, S) == BOUNDS        # ldx < cols
+    assert L.bq_quant_mx(x, rows, cols, 512, v, 512, e, 8, S) == BOUNDS         # lds < cols/32
+    assert L.bq_quant_mx(x, rows, cols, 516, v, 512, e, 16, S) == ALIGN         # ldx % 8
+    assert L.bq_quant_mx(x, rows, cols, 512, v, 520, e, 16, S) == ALIGN         # ldv % 16
+    assert L.bq_quant_mx(x, rows, cols, 512, v, 512, e, 18, S) == ALIGN         # lds % 4
+    assert L.bq_quant_mx(x, rows, cols, 512, v, 512, e + 2, 16, S) == ALIGN     # e8m0 ptr
+    assert L.bq_quant_mx(x, rows, cols, 512, x + 1024, 512, e, 16, S) == ALIAS
+    assert L.bq_quant_mx(None, rows, cols, 512, v, 512, e, 16, S) == NULL
+    assert L.bq_quant_mx(x, 0, cols, 512, v, 512, e, 16, S) == OK
+    assert L.bq_dequant_mx(v, 512, e, 16, rows, cols, v + 64, 512, S) == ALIAS
+    assert L.bq_dequant_mx(v, 512, e, 16, rows, cols, x, 500, S) == BOUNDS
+
+
+def test_mx_slice_errors():
+    rows, cols, total = 16, 256, 1024
+    x, v, e = A, A + 2 ** 20, A + 2 ** 21
+    f = L.bq_quant_mx_slice
+    assert f(x, rows, cols, cols, 64, v, total, e, total // 32, rows, S) == SIZE   # offset % 128
+    assert f(x, rows, 96, cols, 0, v, total, e, total // 32, rows, S) == SIZE      # cols % 128
+    assert f(x, rows, cols, cols, 896, v, total, e, total // 32, rows, S) == BOUNDS  # past ldv
+    assert f(x, rows, cols, cols, 0, v, total, e, total // 32 - 4, rows, S) == BOUNDS
+    assert f(x, rows, cols, cols, 0, v, total, e, total // 32, rows - 1, S) == BOUNDS  # capacity
+    assert f(x, rows, cols, cols, 0, None, total, e, total // 32, rows, S) == NULL
