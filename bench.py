@@ -208,7 +208,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96,
+    ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="rows per rank of the CPU-baseline sample (multiple of 4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
@@ -251,28 +251,33 @@ def main() -> int:
     ms = t0.elapsed_time(t1) / args.steps
     gbs = step.step_bytes / (ms * 1e-3) / 1e9
 
-    # timed region 2: the same work as its primitive launches, HIP events around each
-    nl = len(step.kernels[0])
-    reps = max(1, args.steps // 4)
+    # timed region 2: each distinct kernel of the step alone, R back-to-back launches
+    # (rotating over the input sets) between one pair of HIP events on the launch
+    # stream -- no event sits between two launches, so the average is the kernel's own
+    # duration as a trace shows it.
+    reps = max(10, args.steps // 4)
+    kinds = {}
+    for k, (name, nbytes, _, _) in enumerate(step.kernels[0]):
+        kinds.setdefault((name, nbytes), []).append(k)
     per = {}
-    for i in range(reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(nl)]
-        step.run_kernels(i, ev)
+    for (name, nbytes), idx in kinds.items():
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        for k, (name, nbytes, _, _) in enumerate(step.kernels[i % len(step.kernels)]):
-            key = (name, nbytes)
-            d = per.setdefault(key, {"ms": []})
-            d["ms"].append(ev[k][0].elapsed_time(ev[k][1]))
-    kernels = {}
-    for (name, nbytes), d in per.items():
-        label = f"{name} ({nbytes} B)"
-        us = float(np.mean(d["ms"]) * 1e3)
-        kernels[label] = {"bytes_per_launch": nbytes, "launches_per_step": len(d["ms"]) // reps,
-                          "us_per_launch": us, "gbs": nbytes / (us * 1e-6) / 1e9}
-        kernels[label]["frac"] = kernels[label]["gbs"] / HBM_PEAK_GBS
-        kernels[label]["us_per_step"] = us * kernels[label]["launches_per_step"]
-    per = kernels
+        e0.record(step.stream)
+        for i in range(reps):
+            seq = step.kernels[i % len(step.kernels)]
+            _, _, fn, fargs = seq[idx[i % len(idx)]]
+            st = fn(*fargs)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st}")
+        e1.record(step.stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        per[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_step": len(idx),
+                                       "us_per_launch": us, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                                       "us_per_step": us * len(idx)}
     dom_name = max(per, key=lambda k: per[k]["us_per_step"])
     dom = per[dom_name]
 

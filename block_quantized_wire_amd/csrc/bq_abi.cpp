@@ -5,7 +5,7 @@
 // kernel runs: b12x pull request #241, "[II] Support staged MXFP8 linear inputs",
 // Compatibility).  The library allocates nothing, keeps no state and never
 // synchronizes, so every call may be captured in a HIP graph.
-#include "../../include/blockq.h"
+#include "blockq.h"
 
 #include <hip/hip_runtime.h>
 

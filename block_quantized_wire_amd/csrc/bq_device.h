@@ -23,6 +23,12 @@
 //    |x/s| * 2^-24; with |x/s| <= 127.25 both stay below 2^-15.  Whenever q0 lies
 //    within 2^-13 of a half-integer (or is not finite), the exact IEEE division is
 //    done instead, so round-half-even(q0) == round-half-even(fl32(x/s)) always.
+//
+// Conversions use gfx950's packed instructions, whose rounding is the codecs':
+// v_cvt_pk_bf16_f32 rounds binary32 to bf16 to nearest even (subnormals kept, overflow
+// to infinity); v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3FN code with ties to
+// even and keeps the sign of zero, but turns magnitudes from 464 up into NaN, so its
+// inputs are first clamped to [-448, 448]; v_cvt_pk_f32_fp8 decodes exactly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +44,11 @@ constexpr int kWavesPerGroup = 4;     // 256-thread workgroups
 constexpr int kGroupThreads = 256;
 constexpr int kMaxBatch = 16;
 constexpr int kMaxSrc = 64;
+// Most workgroups of one launch before the waves start walking tiles grid-stride.
+// Measured on MI355X (256 CUs): a grid that covers every tile once streams faster
+// than a persistent grid of 4-16 groups per CU, so the cap only matters for the
+// largest tensors.
+constexpr int kMaxGroups = 256 * 64;
 
 // ---- vector memory ----------------------------------------------------------------
 
@@ -70,13 +81,13 @@ __device__ __forceinline__ void unpack_bf16x8(u32x4 w, float f[8]) {
     f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
-// Round two binary32 values to bf16 (nearest, ties to even; a carry out of the
-// significand moves into the exponent) and pack them, a in the low half.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two binary32 values to bf16 (nearest, ties to even) and pack them, a in the
+// low half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-    ua += 0x7FFFu + ((ua >> 16) & 1u);
-    ub += 0x7FFFu + ((ub >> 16) & 1u);
-    return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ u32x4 pack_bf16x8(const float f[8]) {
@@ -120,19 +131,10 @@ __device__ __forceinline__ float e4m3_block_scale(float amax) {
     return (float)((double)amax * (1.0 / 448.0));
 }
 
-// round-half-even(fl32(x / s)) for |x| <= amax, s = fl32(amax/127) > 0, r ~ 1/s.
-// Returns the integer as a float.  The result never exceeds 127 in magnitude:
-// amax / fl32(amax/127) <= 127 * (1 + 2^-9) even for subnormal scales, so the
-// clamp to [-127, 127] of the definition never changes a value.
-__device__ __forceinline__ float i8_round_quot(float x, float s, float r) {
-    float q0 = x * r;
-    float t = __builtin_rintf(q0);
-    float d = __builtin_fabsf(q0 - t);
-    if (!(d < 0.5f - 0x1.0p-13f))          // near a tie, or not finite: exact path
-        t = __builtin_rintf(x / s);
-    return t;
-}
-
+// Quotient rounding of the block-INT8 rule for |x| <= amax, s = fl32(amax/127):
+// round-half-even(fl32(x / s)) never exceeds 127 in magnitude -- amax / fl32(amax/127)
+// <= 127 * (1 + 2^-9) even for subnormal scales -- so the clamp to [-127, 127] of the
+// definition never changes a value and is not applied.
 // Pack the low bytes of four int-valued floats (in [-127, 127]) into one word.
 __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
     uint32_t ia = (uint32_t)(int)a, ib = (uint32_t)(int)b;
@@ -144,60 +146,109 @@ __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d
 
 // Quantize 8 binary32 values of one lane with its block's scale.  A block whose
 // amax is 0 -- or whose scale underflows to 0, which only binary32 sums can reach --
-// is a zero block: scale 0, payload 0.
+// is a zero block: scale 0, payload 0.  Fast path: q0 = x * rcp(s), rounded to an
+// integer; if any of the lane's 8 quotients lies within 2^-13 of a half-integer, or
+// the scale is below 2^-125 (where rcp(s) may not be finite), the lane's 8 values are
+// redone with the exact IEEE division.  For s >= 2^-125 every q0 is finite.
 __device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
     if (s == 0.0f)
         return u32x2{};
-    float r = __builtin_amdgcn_rcpf(s);
+    const float r = __builtin_amdgcn_rcpf(s);
     float t[8];
+    float dmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-        t[i] = i8_round_quot(f[i], s, r);
+    for (int i = 0; i < 8; ++i) {
+        const float q0 = f[i] * r;
+        t[i] = __builtin_rintf(q0);
+        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(q0 - t[i]));
+    }
+    if (!(s >= 0x1.0p-125f && dmax < 0.5f - 0x1.0p-13f)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = __builtin_rintf(f[i] / s);
+    }
     return u32x2{pack_i8x4(t[0], t[1], t[2], t[3]), pack_i8x4(t[4], t[5], t[6], t[7])};
 }
 
-// Signed bytes of a word as binary32 (exact).
-__device__ __forceinline__ void unpack_i8x4(uint32_t w, float* f) {
-    f[0] = (float)(int)(int8_t)(w & 0xFF);
-    f[1] = (float)(int)(int8_t)((w >> 8) & 0xFF);
-    f[2] = (float)(int)(int8_t)((w >> 16) & 0xFF);
-    f[3] = (float)(int)(int8_t)(w >> 24);
-}
-
-__device__ __forceinline__ void unpack_i8x8(u32x2 w, float f[8]) {
-    unpack_i8x4(w.x, f);
-    unpack_i8x4(w.y, f + 4);
+// Dequantize the 8 signed payload bytes of a lane: f = fl32(q * s).  The bytes are
+// biased to unsigned (q + 128 = byte ^ 0x80) and converted exactly; a fused
+// multiply-add of u * s - 128 * s then rounds the exact product q * s once, which is
+// the binary32 product of the definition, sign of zero included when s > 0 (a zero
+// product then means q = 0, and u * s - 128 * s = +0 = 0 * s).  Other scales -- zero,
+// negative, or s >= 2^120 where 128 * s would overflow -- take the plain
+// convert-and-multiply form.
+__device__ __forceinline__ void dequant_i8x8(u32x2 w, float s, float f[8]) {
+    if (__builtin_expect(s > 0.0f && s < 0x1.0p120f, 1)) {
+        const uint32_t a = w.x ^ 0x80808080u, b = w.y ^ 0x80808080u;
+        const float c = -128.0f * s;
+        f[0] = __builtin_fmaf((float)(a & 0xFFu), s, c);
+        f[1] = __builtin_fmaf((float)((a >> 8) & 0xFFu), s, c);
+        f[2] = __builtin_fmaf((float)((a >> 16) & 0xFFu), s, c);
+        f[3] = __builtin_fmaf((float)(a >> 24), s, c);
+        f[4] = __builtin_fmaf((float)(b & 0xFFu), s, c);
+        f[5] = __builtin_fmaf((float)((b >> 8) & 0xFFu), s, c);
+        f[6] = __builtin_fmaf((float)((b >> 16) & 0xFFu), s, c);
+        f[7] = __builtin_fmaf((float)(b >> 24), s, c);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = (float)(int)(int8_t)((w.x >> (8 * i)) & 0xFFu) * s;
+            f[i + 4] = (float)(int)(int8_t)((w.y >> (8 * i)) & 0xFFu) * s;
+        }
+    }
 }
 
 // ---- OCP E4M3FN ------------------------------------------------------------------------
 
-// E4M3FN encoding of a binary32, round to nearest even, magnitudes >= 448 saturate to
-// 448, sign kept (also of zero).  Written out in integer arithmetic on the bits.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {                 // >= 448
-        code = 0x7E;
-    } else if (a >= 0x3C800000u) {          // >= 2^-6: normal E4M3 range
-        // keep 3 mantissa bits, round half to even on the 20 dropped bits
-        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - ((127u - 7u) << 3);
-    } else {                                // subnormal E4M3: multiples of 2^-9
-        // adding 2^14 leaves a significand grid of 2^-9; RNE happens in the add
-        float t = __uint_as_float(a) + 16384.0f;
-        code = __float_as_uint(t) - 0x46800000u;
-    }
-    return sign | code;
+// E4M3FN codes of four binary32 values packed into a word (a in byte 0): nearest code,
+// ties to even, magnitudes at or above 448 saturate to 448, sign of zero kept.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
-// Exact binary32 value of an E4M3FN code (NaN codes are outside the contract).
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    uint32_t ex = (c >> 3) & 0xFu, man = c & 7u;
-    float mag = (ex == 0) ? (float)man * 0x1.0p-9f
-                          : __uint_as_float(((ex + 120u) << 23) | (man << 20));
-    return (c & 0x80u) ? -mag : mag;
+__device__ __forceinline__ u32x2 e4m3x8(const float f[8]) {
+    return u32x2{e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
+}
+
+// Exact binary32 values of the four E4M3FN codes of a word (byte 0 first).
+__device__ __forceinline__ void e4m3_decode4(uint32_t w, float* f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+}
+
+// E4M3FN codes of fl32(x / s) for the 8 values of a lane, s > 0 the block scale.
+// q0 = x * rcp(s) is within 1.5 * 2^-23 (relative) of x/s and fl32(x/s) within 2^-24,
+// so fl32(x/s) lies inside [q0 (1 - 2^-19), q0 (1 + 2^-19)] (each end rounded once).
+// Rounding to E4M3 is monotone, so when both ends give the same code, so does
+// fl32(x/s); otherwise -- and for scales too small for a finite reciprocal -- the
+// exact IEEE quotients are encoded.
+__device__ __forceinline__ u32x2 e4m3_quot8(const float f[8], float s) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q0 = f[i] * r;
+        lo[i] = q0 * (1.0f - 0x1.0p-19f);
+        hi[i] = q0 * (1.0f + 0x1.0p-19f);
+    }
+    const u32x2 clo = e4m3x8(lo), chi = e4m3x8(hi);
+    if (s >= 0x1.0p-100f && clo.x == chi.x && clo.y == chi.y)
+        return clo;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        t[i] = f[i] / s;
+    return e4m3x8(t);
 }
 
 // MXFP8 shared-scale byte from a bf16 amax given as its 15 magnitude bits: 127 for an

@@ -54,52 +54,58 @@ struct AccumArgs {
     int64_t seg_n;    // values per segment (offset of segment j is j * seg_n)
 };
 
-// Tile bookkeeping common to all INT8 kernels: which block and which 8 values of it
-// this lane owns in tile u of its wave.
-struct LaneMap {
-    int64_t tile0;
-    int sub;      // block index within the tile (= DPP row of the lane)
-    int off;      // first value of the lane within its block
-    bool leader;  // first lane of the row: stores the block's scale
-    __device__ LaneMap(int U) {
+// Lane bookkeeping common to all INT8 kernels: the lane's block within a tile (its DPP
+// row) and its first value in that block.  Waves walk the tiles grid-stride, U adjacent
+// tiles per step, so a launch needs no more workgroups than the chip holds at once.
+struct Lanes {
+    int sub, off;
+    bool leader;     // first lane of the row: stores the block's scale
+    int64_t first;   // first tile of this wave
+    int64_t step;    // tiles between successive steps of this wave
+    __device__ explicit Lanes(int U) {
         const int lane = threadIdx.x & 63;
         const int wave = threadIdx.x >> 6;
-        tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
         sub = lane >> 4;
         off = (lane & 15) * kLaneVals;
         leader = (lane & 15) == 0;
+        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        step = (int64_t)gridDim.x * kWavesPerGroup * U;
     }
-    __device__ int64_t block(int u) const { return (tile0 + u) * kTileBlocks + sub; }
 };
+
+__device__ __forceinline__ int64_t tiles_of(int64_t nb) { return (nb + kTileBlocks - 1) / kTileBlocks; }
 
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
     int8_t* __restrict__ q = a.q[blockIdx.y];
     float* __restrict__ s = a.s[blockIdx.y];
-    const LaneMap L(U);
-    u32x4 xv[U];
+    const Lanes L(U);
+    const int64_t nt = tiles_of(a.nb);
+    for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        u32x4 xv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        xv[u] = (b < a.nb) ? ld16(x + b * kBlock + L.off) : u32x4{};
-    }
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            xv[u] = (b < a.nb) ? ld16(x + b * kBlock + L.off) : u32x4{};
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        float f[8];
-        unpack_bf16x8(xv[u], f);
-        float m = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            float f[8];
+            unpack_bf16x8(xv[u], f);
+            float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-        const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
-        const float sc = i8_scale(amax);
-        const u32x2 qv = quant_i8x8(f, sc);
-        if (b < a.nb) {
-            st8(q + b * kBlock + L.off, qv);
-            if (L.leader)
-                s[b] = sc;
+            for (int i = 0; i < 8; ++i)
+                m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float sc = i8_scale(amax);
+            const u32x2 qv = quant_i8x8(f, sc);
+            if (b < a.nb) {
+                st8(q + b * kBlock + L.off, qv);
+                if (L.leader)
+                    s[b] = sc;
+            }
         }
     }
 }
@@ -109,31 +115,31 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_i8(DequantArgs a) {
     const int8_t* __restrict__ q = a.q[blockIdx.y];
     const float* __restrict__ s = a.s[blockIdx.y];
     uint16_t* __restrict__ y = a.y[blockIdx.y];
-    const LaneMap L(U);
-    u32x2 qv[U];
-    float sv[U];
+    const Lanes L(U);
+    const int64_t nt = tiles_of(a.nb);
+    for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        u32x2 qv[U];
+        float sv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        const bool in = b < a.nb;
-        qv[u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
-        sv[u] = in ? s[b] : 0.0f;
-    }
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            const bool in = b < a.nb;
+            qv[u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
+            sv[u] = in ? s[b] : 0.0f;
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        float f[8];
-        unpack_i8x8(qv[u], f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            f[i] = f[i] * sv[u];
-        if (b < a.nb)
-            st16(y + b * kBlock + L.off, pack_bf16x8(f));
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            float f[8];
+            dequant_i8x8(qv[u], sv[u], f);
+            if (b < a.nb)
+                st16(y + b * kBlock + L.off, pack_bf16x8(f));
+        }
     }
 }
 
-// q_in/q_out and s_in/s_out may be the same buffers: every lane loads its whole share
-// of a block before the block's stores, and no other wave touches that block.
+// q_in/q_out and s_in/s_out may be the same buffers: the lanes of a block load all of
+// it before any of its stores, and no other wave touches that block.
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
     const int8_t* q_in = a.q_in[blockIdx.y];
@@ -141,108 +147,114 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
     const uint16_t* __restrict__ local = a.local[blockIdx.y];
     int8_t* q_out = a.q_out[blockIdx.y];
     float* s_out = a.s_out[blockIdx.y];
-    const LaneMap L(U);
-    u32x2 qv[U];
-    u32x4 lv[U];
-    float sv[U];
+    const Lanes L(U);
+    const int64_t nt = tiles_of(a.nb);
+    for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        u32x2 qv[U];
+        u32x4 lv[U];
+        float sv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        const bool in = b < a.nb;
-        qv[u] = in ? ld8(q_in + b * kBlock + L.off) : u32x2{};
-        sv[u] = in ? s_in[b] : 0.0f;
-        lv[u] = in ? ld16(local + b * kBlock + L.off) : u32x4{};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        float deq[8], loc[8], sum[8];
-        unpack_i8x8(qv[u], deq);
-        unpack_bf16x8(lv[u], loc);
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            deq[i] = deq[i] * sv[u];        // rounded product ...
-            sum[i] = deq[i] + loc[i];       // ... then a rounded add (no contraction)
-            m = __builtin_fmaxf(m, __builtin_fabsf(sum[i]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            const bool in = b < a.nb;
+            qv[u] = in ? ld8(q_in + b * kBlock + L.off) : u32x2{};
+            sv[u] = in ? s_in[b] : 0.0f;
+            lv[u] = in ? ld16(local + b * kBlock + L.off) : u32x4{};
         }
-        const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
-        const float sc = i8_scale(amax);
-        const u32x2 out = quant_i8x8(sum, sc);
-        if (b < a.nb) {
-            st8(q_out + b * kBlock + L.off, out);
-            if (L.leader)
-                s_out[b] = sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            float deq[8], loc[8], sum[8];
+            dequant_i8x8(qv[u], sv[u], deq);        // rounded products ...
+            unpack_bf16x8(lv[u], loc);
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sum[i] = deq[i] + loc[i];            // ... then rounded adds
+                m = __builtin_fmaxf(m, __builtin_fabsf(sum[i]));
+            }
+            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float sc = i8_scale(amax);
+            const u32x2 out = quant_i8x8(sum, sc);
+            if (b < a.nb) {
+                st8(q_out + b * kBlock + L.off, out);
+                if (L.leader)
+                    s_out[b] = sc;
+            }
         }
     }
 }
 
 // Sources are consumed in chunks of 8 whose loads are all issued before the chunk's
-// ordered additions, so up to 8 independent 8-byte streams are in flight per lane.
+// ordered additions, so up to 8 independent streams are in flight per lane.
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     const int64_t seg_off = (int64_t)blockIdx.y * a.seg_n;
     const int64_t seg_sb = seg_off / kBlock;
     uint16_t* __restrict__ y = a.y + seg_off;
-    const LaneMap L(U);
-    float acc[U][8];
+    const Lanes L(U);
+    const int64_t nt = tiles_of(a.nb);
+    for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        float acc[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[u][i] = 0.0f;
-    for (int k0 = 0; k0 < a.nsrc; k0 += 8) {
-        u32x2 qv[8][U];
-        float sv[8][U];
+            for (int i = 0; i < 8; ++i)
+                acc[u][i] = 0.0f;
+        for (int k0 = 0; k0 < a.nsrc; k0 += 8) {
+            u32x2 qv[8][U];
+            float sv[8][U];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (k0 + j < a.nsrc) {
-                const int8_t* q = a.q[k0 + j] + seg_off;
-                const float* s = a.s[k0 + j] + seg_sb;
+            for (int j = 0; j < 8; ++j) {
+                if (k0 + j < a.nsrc) {
+                    const int8_t* q = a.q[k0 + j] + seg_off;
+                    const float* s = a.s[k0 + j] + seg_sb;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t b = L.block(u);
-                    const bool in = b < a.nb;
-                    qv[j][u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
-                    sv[j][u] = in ? s[b] : 0.0f;
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+                        const bool in = b < a.nb;
+                        qv[j][u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
+                        sv[j][u] = in ? s[b] : 0.0f;
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (k0 + j < a.nsrc) {
+            for (int j = 0; j < 8; ++j) {
+                if (k0 + j < a.nsrc) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float f[8];
-                    unpack_i8x8(qv[j][u], f);
+                    for (int u = 0; u < U; ++u) {
+                        float f[8];
+                        dequant_i8x8(qv[j][u], sv[j][u], f);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float term = f[i] * sv[j][u];
-                        acc[u][i] = acc[u][i] + term;
+                        for (int i = 0; i < 8; ++i)
+                            acc[u][i] = acc[u][i] + f[i];
                     }
                 }
             }
         }
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = L.block(u);
-        if (b < a.nb)
-            st16(y + b * kBlock + L.off, pack_bf16x8(acc[u]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            if (b < a.nb)
+                st16(y + b * kBlock + L.off, pack_bf16x8(acc[u]));
+        }
     }
 }
 
-// Launch shape: 256-thread workgroups of 4 waves, each wave U tiles of 4 blocks.
+// Launch shape: 256-thread workgroups of 4 waves, U tiles of 4 blocks per wave step;
+// at most kMaxGroups workgroups in all (the segments of a batch share them).
 template <int U>
 dim3 grid_for(int64_t nb, int count) {
     const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
-    return dim3((unsigned)((nb + per_group - 1) / per_group), (unsigned)count, 1);
+    const int64_t want = (nb + per_group - 1) / per_group;
+    const int64_t cap = kMaxGroups / count > 0 ? kMaxGroups / count : 1;
+    return dim3((unsigned)(want < cap ? want : cap), (unsigned)count, 1);
 }
 
-constexpr int kUQuant = 4;
-constexpr int kUDequant = 4;
+constexpr int kUQuant = 2;
+constexpr int kUDequant = 2;
 constexpr int kUHop = 2;
-constexpr int kUAccum = 1;
+constexpr int kUAccum = 2;
 
 }  // namespace
 

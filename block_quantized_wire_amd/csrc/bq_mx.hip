@@ -49,7 +49,7 @@ struct MxArgs {
 };
 
 struct MxLane {
-    uint32_t row, cb;    // row and 128-column block of the lane's block in tile u
+    uint32_t row, cb;    // row and 128-column block of the lane's block
     bool in;
 };
 
@@ -63,78 +63,89 @@ __device__ __forceinline__ MxLane mx_lane(const MxArgs& a, int64_t tile, int sub
     return m;
 }
 
+// Grid-stride walk over tiles of 4 blocks, U adjacent tiles per wave step.
+struct Walk {
+    int sub, off;
+    int64_t first, step;
+    __device__ explicit Walk(int U) {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        sub = lane >> 4;
+        off = (lane & 15) * kLaneVals;
+        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        step = (int64_t)gridDim.x * kWavesPerGroup * U;
+    }
+};
+
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
+    const Walk w(U);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
-    const int sub = lane >> 4;
-    const int off = (lane & 15) * kLaneVals;
-    u32x4 xv[U];
-    MxLane ml[U];
+    const int64_t nt = ((int64_t)a.nblocks + kTileBlocks - 1) / kTileBlocks;
+    for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
+        u32x4 xv[U];
+        MxLane ml[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        ml[u] = mx_lane(a, tile0 + u, sub);
-        xv[u] = ml[u].in ? ld16(a.x + ml[u].row * a.ldx + ml[u].cb * kBlock + off) : u32x4{};
-    }
+        for (int u = 0; u < U; ++u) {
+            ml[u] = mx_lane(a, t0 + u, w.sub);
+            xv[u] = ml[u].in ? ld16(a.x + ml[u].row * a.ldx + ml[u].cb * kBlock + w.off) : u32x4{};
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float f[8];
-        unpack_bf16x8(xv[u], f);
-        float m = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            float f[8];
+            unpack_bf16x8(xv[u], f);
+            float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-        const uint32_t amax_bits = quad_max4(__float_as_uint(m));
-        const uint32_t byte = e8m0_from_bf16_amax(amax_bits >> 16);
-        const float inv = e8m0_inv_scale(byte);
-        uint32_t c[8];
+            for (int i = 0; i < 8; ++i)
+                m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+            const uint32_t amax_bits = quad_max4(__float_as_uint(m));
+            const uint32_t byte = e8m0_from_bf16_amax(amax_bits >> 16);
+            const float inv = e8m0_inv_scale(byte);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c[i] = e4m3_encode(f[i] * inv);
-        const u32x2 packed{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                           c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-        // gather the 4 group bytes of this 128-column block into the row's first lane
-        const uint32_t word = byte | (dpp<0x104>(byte) << 8) | (dpp<0x108>(byte) << 16) |
-                              (dpp<0x10C>(byte) << 24);
-        if (ml[u].in) {
-            st8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + off, packed);
-            if ((lane & 15) == 0)
-                *reinterpret_cast<uint32_t*>(a.e + ml[u].row * a.lds + ml[u].cb * 4) = word;
+            for (int i = 0; i < 8; ++i)
+                f[i] = f[i] * inv;                 // exact: a power of two
+            const u32x2 codes = e4m3x8(f);
+            // gather the 4 group bytes of this 128-column block into the row's first lane
+            const uint32_t word = byte | (dpp<0x104>(byte) << 8) | (dpp<0x108>(byte) << 16) |
+                                  (dpp<0x10C>(byte) << 24);
+            if (ml[u].in) {
+                st8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off, codes);
+                if ((lane & 15) == 0)
+                    *reinterpret_cast<uint32_t*>(a.e + ml[u].row * a.lds + ml[u].cb * 4) = word;
+            }
         }
     }
 }
 
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_dequant_mx(MxArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
-    const int sub = lane >> 4;
-    const int off = (lane & 15) * kLaneVals;
-    const int grp = (lane & 15) >> 2;
-    u32x2 vv[U];
-    uint32_t ev[U];
-    MxLane ml[U];
+    const Walk w(U);
+    const int grp = (threadIdx.x & 15) >> 2;
+    const int64_t nt = ((int64_t)a.nblocks + kTileBlocks - 1) / kTileBlocks;
+    uint16_t* y = const_cast<uint16_t*>(a.x);
+    for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
+        u32x2 vv[U];
+        uint32_t ev[U];
+        MxLane ml[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        ml[u] = mx_lane(a, tile0 + u, sub);
-        vv[u] = ml[u].in ? ld8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + off) : u32x2{};
-        ev[u] = ml[u].in ? a.e[ml[u].row * a.lds + ml[u].cb * 4 + grp] : 127u;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        // 2^(byte-127): a normal binary32 for byte >= 1, the subnormal 2^-127 for byte 0
-        const float sc = __uint_as_float(ev[u] ? (ev[u] << 23) : 0x00400000u);
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = e4m3_decode((vv[u].x >> (8 * i)) & 0xFFu) * sc;
-            f[i + 4] = e4m3_decode((vv[u].y >> (8 * i)) & 0xFFu) * sc;
+        for (int u = 0; u < U; ++u) {
+            ml[u] = mx_lane(a, t0 + u, w.sub);
+            vv[u] = ml[u].in ? ld8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off) : u32x2{};
+            ev[u] = ml[u].in ? a.e[ml[u].row * a.lds + ml[u].cb * 4 + grp] : 127u;
         }
-        if (ml[u].in)
-            st16(const_cast<uint16_t*>(a.x) + ml[u].row * a.ldx + ml[u].cb * kBlock + off,
-                 pack_bf16x8(f));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // 2^(byte-127): a normal binary32 for byte >= 1, the subnormal 2^-127 for byte 0
+            const float sc = __uint_as_float(ev[u] ? (ev[u] << 23) : 0x00400000u);
+            float f[8];
+            e4m3_decode4(vv[u].x, f);
+            e4m3_decode4(vv[u].y, f + 4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[i] = f[i] * sc;
+            if (ml[u].in)
+                st16(y + ml[u].row * a.ldx + ml[u].cb * kBlock + w.off, pack_bf16x8(f));
+        }
     }
 }
 
@@ -143,44 +154,34 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_e4m3_b128(const uint16_
                                                                   uint8_t* __restrict__ v,
                                                                   float* __restrict__ s,
                                                                   int64_t nb) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
-    const int sub = lane >> 4;
-    const int off = (lane & 15) * kLaneVals;
-    u32x4 xv[U];
+    const Walk w(U);
+    const bool leader = (threadIdx.x & 15) == 0;
+    const int64_t nt = (nb + kTileBlocks - 1) / kTileBlocks;
+    for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
+        u32x4 xv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = (tile0 + u) * kTileBlocks + sub;
-        xv[u] = (b < nb) ? ld16(x + b * kBlock + off) : u32x4{};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = (tile0 + u) * kTileBlocks + sub;
-        float f[8];
-        unpack_bf16x8(xv[u], f);
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-        const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
-        const float sc = e4m3_block_scale(amax);
-        uint32_t c[8];
-        if (sc == 0.0f) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                c[i] = 0u;                    // zero block: every byte 0x00
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                c[i] = e4m3_encode(f[i] / sc);
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
+            xv[u] = (b < nb) ? ld16(x + b * kBlock + w.off) : u32x4{};
         }
-        const u32x2 packed{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                           c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-        if (b < nb) {
-            st8(v + b * kBlock + off, packed);
-            if ((lane & 15) == 0)
-                s[b] = sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
+            float f[8];
+            unpack_bf16x8(xv[u], f);
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float sc = e4m3_block_scale(amax);
+            // zero block: every byte 0x00 (negative zeros included)
+            const u32x2 codes = (sc == 0.0f) ? u32x2{} : e4m3_quot8(f, sc);
+            if (b < nb) {
+                st8(v + b * kBlock + w.off, codes);
+                if (leader)
+                    s[b] = sc;
+            }
         }
     }
 }
@@ -190,42 +191,42 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_e4m3_b128(const uint8
                                                                     const float* __restrict__ s,
                                                                     uint16_t* __restrict__ y,
                                                                     int64_t nb) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
-    const int sub = lane >> 4;
-    const int off = (lane & 15) * kLaneVals;
-    u32x2 vv[U];
-    float sv[U];
+    const Walk w(U);
+    const int64_t nt = (nb + kTileBlocks - 1) / kTileBlocks;
+    for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
+        u32x2 vv[U];
+        float sv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = (tile0 + u) * kTileBlocks + sub;
-        const bool in = b < nb;
-        vv[u] = in ? ld8(v + b * kBlock + off) : u32x2{};
-        sv[u] = in ? s[b] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t b = (tile0 + u) * kTileBlocks + sub;
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = e4m3_decode((vv[u].x >> (8 * i)) & 0xFFu) * sv[u];
-            f[i + 4] = e4m3_decode((vv[u].y >> (8 * i)) & 0xFFu) * sv[u];
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
+            const bool in = b < nb;
+            vv[u] = in ? ld8(v + b * kBlock + w.off) : u32x2{};
+            sv[u] = in ? s[b] : 0.0f;
         }
-        if (b < nb)
-            st16(y + b * kBlock + off, pack_bf16x8(f));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
+            float f[8];
+            e4m3_decode4(vv[u].x, f);
+            e4m3_decode4(vv[u].y, f + 4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[i] = f[i] * sv[u];
+            if (b < nb)
+                st16(y + b * kBlock + w.off, pack_bf16x8(f));
+        }
     }
 }
 
 template <int U>
 unsigned groups_for(int64_t nb) {
     const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
-    return (unsigned)((nb + per_group - 1) / per_group);
+    const int64_t want = (nb + per_group - 1) / per_group;
+    return (unsigned)(want < kMaxGroups ? want : kMaxGroups);
 }
 
-constexpr int kUMx = 4;
-constexpr int kUE4 = 4;
+constexpr int kUMx = 2;
+constexpr int kUE4 = 2;
 
 }  // namespace
 
