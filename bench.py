@@ -249,7 +249,7 @@ def main() -> int:
     t1.record(step.stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    gbs = step.step_bytes / (ms * 1e-3) / 1e9
+    step_gbs = step.step_bytes / (ms * 1e-3) / 1e9
 
     # timed region 2: each distinct kernel of the step alone, R back-to-back launches
     # (rotating over the input sets) between one pair of HIP events on the launch
@@ -281,6 +281,28 @@ def main() -> int:
     dom_name = max(per, key=lambda k: per[k]["us_per_step"])
     dom = per[dom_name]
 
+    # accuracy on input set 0, outside the timed regions: the all-reduce outputs against
+    # the exact (fp64) sum of the bf16 partials, the codec round trips against their input
+    step.run(0)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.view(torch.bfloat16).double().reshape(-1)
+    exact = sum(f64(p) for p in step.parts[0])
+
+    def err(got, ref):
+        d = (got - ref).abs()
+        return {"max_abs": float(d.max()), "rms": float(d.pow(2).mean().sqrt())}
+
+    mx_in = torch.cat([p.view(ROWS, COLS) for p in step.parts[0]], dim=1)
+    accuracy = {
+        "i8_ring_vs_fp64_sum": err(f64(step.ring_out[0]), exact),
+        "i8_a2a_vs_fp64_sum": err(f64(step.a2a_out[0]), exact),
+        "mxfp8_roundtrip": err(f64(step.mx_y.contiguous()), f64(mx_in.contiguous())),
+        "e4m3_b128_roundtrip": err(f64(step.e4_y), f64(step.parts[0][0])),
+        "ranks_bit_identical": all(torch.equal(step.ring_out[0], o) for o in step.ring_out) and
+        all(torch.equal(step.a2a_out[0], o) for o in step.a2a_out),
+    }
+    del exact, mx_in
+
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
@@ -291,9 +313,9 @@ def main() -> int:
 
     line = {
         "metric": METRIC,
-        "value": round(gbs, 1),
+        "value": round(step_gbs, 1),
         "unit": "GB/s",
-        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "pct_of_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -317,6 +339,7 @@ def main() -> int:
                         "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
                         "frac": round(v["frac"], 4)} for k, v in per.items()},
     }
+    line["accuracy"] = accuracy
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_rows)
         cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9

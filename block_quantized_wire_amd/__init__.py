@@ -68,6 +68,10 @@ def _L() -> ctypes.CDLL:
     """The loaded libblockq.so (loaded on first use; a missing library is an error)."""
     global _lib
     if _lib is None:
+        # torch brings its own HIP runtime (same soname, libamdhip64.so.7).  Loading it
+        # first makes libblockq.so bind to that one runtime; loaded the other way round,
+        # the process would hold two HIP runtimes and ours would see no device.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python block_quantized_wire_amd/build.py` (hipcc, gfx950)")

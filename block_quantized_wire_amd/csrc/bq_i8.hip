@@ -267,9 +267,7 @@ hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q
         a.s[i] = s[i];
     }
     a.nb = n / kBlock;
-    hipLaunchKernelGGL(k_quant_i8<kUQuant>, grid_for<kUQuant>(a.nb, count), dim3(kGroupThreads),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch1(k_quant_i8<kUQuant>, grid_for<kUQuant>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
@@ -281,9 +279,7 @@ hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* con
         a.y[i] = y[i];
     }
     a.nb = n / kBlock;
-    hipLaunchKernelGGL(k_dequant_i8<kUDequant>, grid_for<kUDequant>(a.nb, count),
-                       dim3(kGroupThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch1(k_dequant_i8<kUDequant>, grid_for<kUDequant>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
@@ -298,9 +294,7 @@ hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float*
         a.s_out[i] = s_out[i];
     }
     a.nb = n / kBlock;
-    hipLaunchKernelGGL(k_ring_hop_i8<kUHop>, grid_for<kUHop>(a.nb, count), dim3(kGroupThreads),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch1(k_ring_hop_i8<kUHop>, grid_for<kUHop>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
@@ -314,9 +308,7 @@ hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const*
     a.nsrc = nsrc;
     a.nb = seg_n / kBlock;
     a.seg_n = seg_n;
-    hipLaunchKernelGGL(k_accum_i8<kUAccum>, grid_for<kUAccum>(a.nb, nseg), dim3(kGroupThreads),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch1(k_accum_i8<kUAccum>, grid_for<kUAccum>(a.nb, nseg), dim3(kGroupThreads), stream, a);
 }
 
 }  // namespace bq

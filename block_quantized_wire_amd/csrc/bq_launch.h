@@ -10,6 +10,15 @@
 
 namespace bq {
 
+// Launch `kernel` with its one by-value argument struct on `stream` and return the
+// status of this launch itself (not the thread's sticky last error, which may hold
+// an earlier failure of some unrelated runtime call).
+template <typename Arg>
+hipError_t launch1(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, Arg arg) {
+    void* args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+}
+
 // Block INT8.  Segment i of a batch is (x[i] -> q[i], s[i]), n values each.
 hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
                            float* const* s, int64_t n, hipStream_t stream);

@@ -149,11 +149,19 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_mx(MxArgs a) {
     }
 }
 
+struct E4Args {
+    const uint16_t* x;   // quantize input / dequantize output (as bf16 bits)
+    uint8_t* v;
+    float* s;
+    int64_t nb;
+};
+
 template <int U>
-__global__ __launch_bounds__(kGroupThreads) void k_quant_e4m3_b128(const uint16_t* __restrict__ x,
-                                                                  uint8_t* __restrict__ v,
-                                                                  float* __restrict__ s,
-                                                                  int64_t nb) {
+__global__ __launch_bounds__(kGroupThreads) void k_quant_e4m3_b128(E4Args a) {
+    const uint16_t* __restrict__ x = a.x;
+    uint8_t* __restrict__ v = a.v;
+    float* __restrict__ s = a.s;
+    const int64_t nb = a.nb;
     const Walk w(U);
     const bool leader = (threadIdx.x & 15) == 0;
     const int64_t nt = (nb + kTileBlocks - 1) / kTileBlocks;
@@ -187,10 +195,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_e4m3_b128(const uint16_
 }
 
 template <int U>
-__global__ __launch_bounds__(kGroupThreads) void k_dequant_e4m3_b128(const uint8_t* __restrict__ v,
-                                                                    const float* __restrict__ s,
-                                                                    uint16_t* __restrict__ y,
-                                                                    int64_t nb) {
+__global__ __launch_bounds__(kGroupThreads) void k_dequant_e4m3_b128(E4Args a) {
+    const uint8_t* __restrict__ v = a.v;
+    const float* __restrict__ s = a.s;
+    uint16_t* __restrict__ y = const_cast<uint16_t*>(a.x);
+    const int64_t nb = a.nb;
     const Walk w(U);
     const int64_t nt = (nb + kTileBlocks - 1) / kTileBlocks;
     for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
@@ -242,9 +251,7 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
     a.lds = lds;
     a.nblocks = (uint32_t)(rows * (cols / kBlock));
     a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
-    hipLaunchKernelGGL(k_quant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch1(k_quant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
@@ -259,25 +266,21 @@ hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
     a.lds = lds;
     a.nblocks = (uint32_t)(rows * (cols / kBlock));
     a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
-    hipLaunchKernelGGL(k_dequant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch1(k_dequant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_quant_e4m3_b128(const uint16_t* x, uint8_t* v, float* s, int64_t n,
                                   hipStream_t stream) {
-    const int64_t nb = n / kBlock;
-    hipLaunchKernelGGL(k_quant_e4m3_b128<kUE4>, dim3(groups_for<kUE4>(nb)), dim3(kGroupThreads),
-                       0, stream, x, v, s, nb);
-    return hipGetLastError();
+    const E4Args a{x, v, s, n / kBlock};
+    return launch1(k_quant_e4m3_b128<kUE4>, dim3(groups_for<kUE4>(a.nb)), dim3(kGroupThreads),
+                   stream, a);
 }
 
 hipError_t launch_dequant_e4m3_b128(const uint8_t* v, const float* s, uint16_t* y, int64_t n,
                                     hipStream_t stream) {
-    const int64_t nb = n / kBlock;
-    hipLaunchKernelGGL(k_dequant_e4m3_b128<kUE4>, dim3(groups_for<kUE4>(nb)),
-                       dim3(kGroupThreads), 0, stream, v, s, y, nb);
-    return hipGetLastError();
+    const E4Args a{y, const_cast<uint8_t*>(v), const_cast<float*>(s), n / kBlock};
+    return launch1(k_dequant_e4m3_b128<kUE4>, dim3(groups_for<kUE4>(a.nb)), dim3(kGroupThreads),
+                   stream, a);
 }
 
 }  // namespace bq
