@@ -18,11 +18,17 @@
 //    argument with period 3 covers a/448 = (a/7) * 2^-6 for bf16 a (no exact
 //    midpoint is reachable from a bf16 numerator there either).
 //
-//  * Element quotients.  q0 = x * rcp(s) differs from x/s by at most
-//    |x/s| * 1.5 * 2^-23 (v_rcp_f32 is accurate to 1 ulp) and fl32(x/s) from x/s by
-//    |x/s| * 2^-24; with |x/s| <= 127.25 both stay below 2^-15.  Whenever q0 lies
-//    within 2^-13 of a half-integer (or is not finite), the exact IEEE division is
-//    done instead, so round-half-even(q0) == round-half-even(fl32(x/s)) always.
+//  * Element quotients.  fl32(x/s) == fl32(fl64(x) * r) for fp32 x, s whenever r is
+//    within 2^-52 (relative) of 1/s and x/s is a normal binary32: write x = X 2^a,
+//    s = S 2^b with integer significands X, S < 2^24.  A binary32 rounding midpoint m
+//    has an odd 25-bit significand, so x/s == m would need X's odd part to be a
+//    multiple of a number >= 2^24 + 1, which it is not; otherwise |x/s - m| is at
+//    least 2^-49 (relative), because the difference is a nonzero integer over S 2^25.
+//    The fp64 product errs by less than 2^-51, so it rounds to the same binary32.
+//    Quotients below the normal range round to 0 (INT8) or to a zero E4M3 code of the
+//    right sign either way.  r is rcp(s) in fp64 refined by two Newton steps.
+//    On MI355X non-packed fp32 and fp64 instructions issue at the same rate, so this
+//    costs about what a reciprocal multiply plus a near-tie check did, with no branch.
 //
 // Conversions use gfx950's packed instructions, whose rounding is the codecs':
 // v_cvt_pk_bf16_f32 rounds binary32 to bf16 to nearest even (subnormals kept, overflow
@@ -149,29 +155,30 @@ __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d
     return lo | hi;
 }
 
+// fl64(1/s) to within 2^-52 (relative) for a positive finite binary32 s: the hardware
+// fp64 reciprocal refined by two Newton-Raphson steps (each squares the error).
+__device__ __forceinline__ double recip64(float s) {
+    const double d = (double)s;
+    double r = __builtin_amdgcn_rcp(d);
+    r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+    r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+    return r;
+}
+
+// fl32(x / s) exactly (see the header comment), given r = recip64(s).
+__device__ __forceinline__ float quot32(float x, double r) { return (float)((double)x * r); }
+
 // Quantize 8 binary32 values of one lane with its block's scale.  A block whose
 // amax is 0 -- or whose scale underflows to 0, which only binary32 sums can reach --
-// is a zero block: scale 0, payload 0.  Fast path: q0 = x * rcp(s), rounded to an
-// integer; if any of the lane's 8 quotients lies within 2^-13 of a half-integer, or
-// the scale is below 2^-125 (where rcp(s) may not be finite), the lane's 8 values are
-// redone with the exact IEEE division.  For s >= 2^-125 every q0 is finite.
+// is a zero block: scale 0, payload 0.
 __device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
     if (s == 0.0f)
         return u32x2{};
-    const float r = __builtin_amdgcn_rcpf(s);
+    const double r = recip64(s);
     float t[8];
-    float dmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q0 = f[i] * r;
-        t[i] = __builtin_rintf(q0);
-        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(q0 - t[i]));
-    }
-    if (!(s >= 0x1.0p-125f && dmax < 0.5f - 0x1.0p-13f)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            t[i] = __builtin_rintf(f[i] / s);
-    }
+    for (int i = 0; i < 8; ++i)
+        t[i] = __builtin_rintf(quot32(f[i], r));
     return u32x2{pack_i8x4(t[0], t[1], t[2], t[3]), pack_i8x4(t[4], t[5], t[6], t[7])};
 }
 
@@ -231,28 +238,14 @@ __device__ __forceinline__ void e4m3_decode4(uint32_t w, float* f) {
     f[3] = hi.y;
 }
 
-// E4M3FN codes of fl32(x / s) for the 8 values of a lane, s > 0 the block scale.
-// q0 = x * rcp(s) is within 1.5 * 2^-23 (relative) of x/s and fl32(x/s) within 2^-24,
-// so fl32(x/s) lies inside [q0 (1 - 2^-19), q0 (1 + 2^-19)] (each end rounded once).
-// Rounding to E4M3 is monotone, so when both ends give the same code, so does
-// fl32(x/s); otherwise -- and for scales too small for a finite reciprocal -- the
-// exact IEEE quotients are encoded.
+// E4M3FN codes of fl32(x / s) for the 8 values of a lane, s > 0 the block scale; the
+// binary32 quotients are exact (see the header comment).
 __device__ __forceinline__ u32x2 e4m3_quot8(const float f[8], float s) {
-    const float r = __builtin_amdgcn_rcpf(s);
-    float lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q0 = f[i] * r;
-        lo[i] = q0 * (1.0f - 0x1.0p-19f);
-        hi[i] = q0 * (1.0f + 0x1.0p-19f);
-    }
-    const u32x2 clo = e4m3x8(lo), chi = e4m3x8(hi);
-    if (s >= 0x1.0p-100f && clo.x == chi.x && clo.y == chi.y)
-        return clo;
+    const double r = recip64(s);
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        t[i] = f[i] / s;
+        t[i] = quot32(f[i], r);
     return e4m3x8(t);
 }
 
