@@ -5,8 +5,9 @@ A step is one pass of the whole hot path over one batch of synthetic input: four
 simulated ranks, each holding a 3072x7168 bf16 partial (N(0, 0.5)), go through
   * the i8_ring all-reduce: block-INT8 quantize, three fused ring-hop steps, and
     every rank's materialization from the final payloads;
-  * the i8_a2a all-reduce: quantize once, 4-source FP32 accumulate per owner,
-    requantize, every rank's materialization;
+  * the i8_a2a all-reduce: quantize once, then per owner one fused pass (4-source
+    FP32 accumulate, bf16 rounding, requantize, the owner's own materialization),
+    then the other ranks' materialization of every shard;
   * MXFP8: the four partials staged as 128-aligned slices of a 3072x28672 buffer,
     then dequantized;
   * the E4M3 128-block codec on rank 0's partial, quantize and dequantize.
@@ -50,6 +51,8 @@ B_DEQUANT = 132 + 256
 B_DEQUANT_SHARED = lambda w: 132 + 256 * w   # w ranks materialize from one shared payload
 B_HOP = 132 + 256 + 132    # payload + local bf16 in; payload out
 B_ACCUM = lambda w: 132 * w + 256
+B_A2A_REDUCE = lambda w: 132 * w + 132 + 256   # w sources in; payload + owner's bf16 out
+B_ALLGATHER_SKIP = lambda w: 132 + 256 * (w - 1)   # shared payload once; w-1 ranks write
 B_MX = 256 + 128 + 4       # bf16 in; E4M3 + 4 E8M0 bytes out (per 128 values)
 B_E4M3 = 256 + 132
 
@@ -120,28 +123,25 @@ class Step:
                 sk = A([P(b["s_wire"]) + 4 * MB * chunk(r, k) for r in range(W)])
                 kern.append(("ring_hop_i8 x4", NB * B_HOP, L.bq_ring_hop_i8_batch,
                              (W, qk, sk, lk, M, qk, sk, sp)))
-            kern.append(("dequant_i8 x4 shared payload", NB * B_DEQUANT_SHARED(W),
-                         L.bq_dequant_i8_batch,
-                         (W, A([P(b["q_wire"])] * W), A([P(b["s_wire"])] * W), N,
-                          A([P(t) for t in b["ring_out"]]), sp)))
-            # i8_a2a driver and its kernels
-            a2a_bytes = (W * NB * B_QUANT + W * MB * B_ACCUM(W) + NB * B_QUANT
-                         + NB * B_DEQUANT_SHARED(W))
+            kern.append(("allgather_dequant_i8 x4", NB * B_DEQUANT_SHARED(W),
+                         L.bq_allgather_dequant_i8,
+                         (W, P(b["q_wire"]), P(b["s_wire"]), N, A([P(t) for t in b["ring_out"]]),
+                          0, sp)))
+            # i8_a2a driver and its kernels: quantize once, fused owner step (payload and
+            # the owner's own shard), the other ranks' materialization of each shard
+            a2a_bytes = (W * NB * B_QUANT + NB * B_A2A_REDUCE(W) + NB * B_ALLGATHER_SKIP(W))
             qsend, ssend = A([P(t) for t in b["q_send"]]), A([P(t) for t in b["s_send"]])
+            outs = A([P(t) for t in b["a2a_out"]])
             calls.append(("i8_a2a_allreduce", a2a_bytes,
-                          L.bq_a2a_allreduce_i8, (W, N, xs, qsend, ssend, P(b["red"]), P(b["q_bc"]),
-                                                  P(b["s_bc"]), A([P(t) for t in b["a2a_out"]]),
-                                                  sp)))
+                          L.bq_a2a_allreduce_i8, (W, N, xs, qsend, ssend, None, P(b["q_bc"]),
+                                                  P(b["s_bc"]), outs, sp)))
             kern.append(("quant_i8 x4", W * NB * B_QUANT, L.bq_quant_i8_batch,
                          (W, xs, N, qsend, ssend, sp)))
-            kern.append(("accum_i8 4src x4", W * MB * B_ACCUM(W), L.bq_dequant_accum_i8_batch,
-                         (W, W, qsend, ssend, M, P(b["red"]), sp)))
-            kern.append(("quant_i8 x1", NB * B_QUANT, L.bq_quant_i8_batch,
-                         (1, A([P(b["red"])]), N, A([P(b["q_bc"])]), A([P(b["s_bc"])]), sp)))
-            kern.append(("dequant_i8 x4 shared payload", NB * B_DEQUANT_SHARED(W),
-                         L.bq_dequant_i8_batch,
-                         (W, A([P(b["q_bc"])] * W), A([P(b["s_bc"])] * W), N,
-                          A([P(t) for t in b["a2a_out"]]), sp)))
+            own = A([P(b["a2a_out"][j]) + 2 * M * j for j in range(W)])
+            kern.append(("a2a_reduce_i8 4src x4 owners", NB * B_A2A_REDUCE(W), L.bq_a2a_reduce_i8,
+                         (W, W, qsend, ssend, M, P(b["q_bc"]), P(b["s_bc"]), own, None, sp)))
+            kern.append(("allgather_dequant_i8 x4 skip own", NB * B_ALLGATHER_SKIP(W),
+                         L.bq_allgather_dequant_i8, (W, P(b["q_bc"]), P(b["s_bc"]), N, outs, 1, sp)))
             # MXFP8: the four partials as 128-aligned slices of the staging buffer
             for r in range(W):
                 c = ("quant_mx_slice", NB * B_MX, L.bq_quant_mx_slice,

@@ -19,9 +19,10 @@ import os
 __all__ = [
     "BlockqError", "lib", "LIB_PATH",
     "bq_quant_i8", "bq_dequant_i8", "bq_dequant_accum_i8", "bq_dequant_accum_i8_batch",
+    "bq_a2a_reduce_i8",
     "bq_ring_hop_i8",
     "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
-    "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
+    "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
     "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
     "bq_quant_e4m3_b128", "bq_dequant_e4m3_b128",
     "bq_wire_bytes_b128", "bq_status_str", "bq_version",
@@ -48,10 +49,12 @@ _SIGS = {
     "bq_dequant_i8": [_P, _P, _I64, _P, _P],
     "bq_dequant_accum_i8": [_I, _PP, _PP, _I64, _P, _P],
     "bq_dequant_accum_i8_batch": [_I, _I, _PP, _PP, _I64, _P, _P],
+    "bq_a2a_reduce_i8": [_I, _I, _PP, _PP, _I64, _P, _P, _PP, _P, _P],
     "bq_ring_hop_i8": [_P, _P, _P, _I64, _P, _P, _P],
     "bq_quant_i8_batch": [_I, _PP, _I64, _PP, _PP, _P],
     "bq_dequant_i8_batch": [_I, _PP, _PP, _I64, _PP, _P],
     "bq_ring_hop_i8_batch": [_I, _PP, _PP, _PP, _I64, _PP, _PP, _P],
+    "bq_allgather_dequant_i8": [_I, _P, _P, _I64, _PP, _I, _P],
     "bq_ring_allreduce_i8": [_I, _I64, _PP, _P, _P, _PP, _P],
     "bq_a2a_allreduce_i8": [_I, _I64, _PP, _PP, _PP, _P, _P, _P, _PP, _P],
     "bq_quant_mx": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
@@ -156,6 +159,15 @@ def bq_dequant_accum_i8_batch(nseg: int, q_srcs, s_srcs, y, seg_n: int | None = 
                                          _ptr(y), _stream(stream)))
 
 
+def bq_a2a_reduce_i8(nseg: int, q_srcs, s_srcs, q_out, s_out, y_out=None, red=None,
+                     seg_n: int | None = None, stream=None) -> None:
+    seg_n = _numel(q_out) // nseg if seg_n is None else seg_n
+    ys = _ptrs(y_out) if y_out is not None else None
+    _check("bq_a2a_reduce_i8",
+           _L().bq_a2a_reduce_i8(nseg, len(q_srcs), _ptrs(q_srcs), _ptrs(s_srcs), seg_n,
+                                 _ptr(q_out), _ptr(s_out), ys, _ptr(red), _stream(stream)))
+
+
 def bq_ring_hop_i8(q_in, s_in, local, q_out, s_out, n: int | None = None, stream=None) -> None:
     n = _numel(local) if n is None else n
     _check("bq_ring_hop_i8", _L().bq_ring_hop_i8(_ptr(q_in), _ptr(s_in), _ptr(local), n,
@@ -180,6 +192,14 @@ def bq_ring_hop_i8_batch(q_in, s_in, local, q_out, s_out, n: int | None = None,
     _check("bq_ring_hop_i8_batch",
            _L().bq_ring_hop_i8_batch(len(q_in), _ptrs(q_in), _ptrs(s_in), _ptrs(local), n,
                                     _ptrs(q_out), _ptrs(s_out), _stream(stream)))
+
+
+def bq_allgather_dequant_i8(q, s, outs, skip_own: bool = False, n: int | None = None,
+                            stream=None) -> None:
+    n = _numel(q) if n is None else n
+    _check("bq_allgather_dequant_i8",
+           _L().bq_allgather_dequant_i8(len(outs), _ptr(q), _ptr(s), n, _ptrs(outs), int(skip_own),
+                                        _stream(stream)))
 
 
 def bq_ring_allreduce_i8(partials, q_wire, s_wire, outs, n: int | None = None,

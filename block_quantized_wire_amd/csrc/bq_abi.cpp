@@ -253,7 +253,78 @@ bq_status bq_dequant_accum_i8(int nsrc, const int8_t* const* q_srcs, const float
     return bq_dequant_accum_i8_batch(1, nsrc, q_srcs, s_srcs, n, y, stream);
 }
 
+bq_status bq_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
+                           const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
+                           float* s_out, uint16_t* const* y_out, uint16_t* red, void* stream) {
+    if (nsrc < 1 || nsrc > BQ_MAX_SRC || nseg < 1 || nseg > BQ_MAX_BATCH)
+        return BQ_ERR_NSRC;
+    BQ_TRY(check_n(seg_n));
+    if (seg_n == 0)
+        return BQ_OK;
+    if (!q_srcs || !s_srcs)
+        return BQ_ERR_NULL;
+    const int64_t n = seg_n * nseg, sb = 4 * (n / kBlk);
+    BQ_TRY(check_payload(q_out));
+    BQ_TRY(check_scales(s_out));
+    Span outs[BQ_MAX_BATCH + 3];
+    int no = 0;
+    outs[no++] = span(q_out, n);
+    outs[no++] = span(s_out, sb);
+    if (red) {
+        BQ_TRY(check_bf16(red));
+        outs[no++] = span(red, 2 * n);
+    }
+    if (y_out) {
+        for (int j = 0; j < nseg; ++j) {
+            BQ_TRY(check_bf16(y_out[j]));
+            outs[no++] = span(y_out[j], 2 * seg_n);
+        }
+    }
+    Span ins[2 * BQ_MAX_SRC];
+    for (int k = 0; k < nsrc; ++k) {
+        BQ_TRY(check_payload(q_srcs[k]));
+        BQ_TRY(check_scales(s_srcs[k]));
+        ins[2 * k] = span(q_srcs[k], n);
+        ins[2 * k + 1] = span(s_srcs[k], sb);
+    }
+    if (any_overlap(outs, no, ins, 2 * nsrc))
+        return BQ_ERR_ALIAS;
+    return launched(bq::launch_a2a_reduce_i8(nsrc, q_srcs, s_srcs, nseg, seg_n, q_out, s_out,
+                                             y_out, red, as_stream(stream)));
+}
+
 // ---- collectives on one GPU ------------------------------------------------------------
+
+bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, int64_t n,
+                                  uint16_t* const* out, int skip_own, void* stream) {
+    const int W = world;
+    if (W < 1 || W > BQ_MAX_BATCH)
+        return BQ_ERR_NSRC;
+    BQ_TRY(check_n(n));
+    if (n % (kBlk * W) != 0)
+        return BQ_ERR_SIZE;
+    if (n == 0)
+        return BQ_OK;
+    if (!out)
+        return BQ_ERR_NULL;
+    BQ_TRY(check_payload(q));
+    BQ_TRY(check_scales(s));
+    Span outs[BQ_MAX_BATCH], ins[2] = {span(q, n), span(s, 4 * (n / kBlk))};
+    for (int r = 0; r < W; ++r) {
+        BQ_TRY(check_bf16(out[r]));
+        outs[r] = span(out[r], 2 * n);
+    }
+    if (any_overlap(outs, W, ins, 2))
+        return BQ_ERR_ALIAS;
+    const int8_t* qi[BQ_MAX_BATCH];
+    const float* si[BQ_MAX_BATCH];
+    for (int r = 0; r < W; ++r) {
+        qi[r] = q;
+        si[r] = s;
+    }
+    return launched(bq::launch_dequant_i8(W, qi, si, out, n, as_stream(stream),
+                                          skip_own ? n / W : 0));
+}
 
 bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
                                int8_t* q_wire, float* s_wire, uint16_t* const* out,
@@ -332,7 +403,8 @@ bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* parti
         return BQ_OK;
     if (!partials || !q_send || !s_send || !out)
         return BQ_ERR_NULL;
-    BQ_TRY(check_bf16(red));
+    if (red)
+        BQ_TRY(check_bf16(red));
     BQ_TRY(check_payload(q_bcast));
     BQ_TRY(check_scales(s_bcast));
     const int64_t sb = 4 * (n / kBlk);
@@ -348,7 +420,8 @@ bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* parti
         outs[no++] = span(s_send[r], sb);
         outs[no++] = span(out[r], 2 * n);
     }
-    outs[no++] = span(red, 2 * n);
+    if (red)
+        outs[no++] = span(red, 2 * n);
     outs[no++] = span(q_bcast, n);
     outs[no++] = span(s_bcast, sb);
     if (any_overlap(outs, no, ins, W))
@@ -358,21 +431,23 @@ bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* parti
     const int64_t m = n / W;
     // quantize every partial once
     bq_status stt = launched(bq::launch_quant_i8(W, partials, q_send, s_send, n, st));
-    // owner j accumulates shard j of every payload, in rank order
+    // owner j accumulates shard j of every payload in rank order, requantizes its bf16
+    // sum once into the broadcast payload and materializes its own shard from it
+    uint16_t* own[BQ_MAX_BATCH];
+    for (int j = 0; j < W; ++j)
+        own[j] = out[j] + j * m;
     if (stt == BQ_OK)
-        stt = launched(bq::launch_accum_i8(W, q_send, s_send, red, W, m, st));
-    // requantize the owners' bf16 sums once (the broadcast payload)
-    if (stt == BQ_OK)
-        stt = launched(bq::launch_quant_i8(1, &red, &q_bcast, &s_bcast, n, st));
-    // every rank materializes every shard from the broadcast payload
-    if (stt == BQ_OK) {
+        stt = launched(bq::launch_a2a_reduce_i8(W, q_send, s_send, W, m, q_bcast, s_bcast, own,
+                                                red, st));
+    // every rank materializes the other owners' shards from the broadcast payload
+    if (stt == BQ_OK && W > 1) {
         const int8_t* qi[BQ_MAX_BATCH];
         const float* si[BQ_MAX_BATCH];
         for (int r = 0; r < W; ++r) {
             qi[r] = q_bcast;
             si[r] = s_bcast;
         }
-        stt = launched(bq::launch_dequant_i8(W, qi, si, out, n, st));
+        stt = launched(bq::launch_dequant_i8(W, qi, si, out, n, st, m));
     }
     return stt;
 }

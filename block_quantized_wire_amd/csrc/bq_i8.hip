@@ -34,6 +34,7 @@ struct DequantArgs {
     const float* s[kMaxBatch];
     uint16_t* y[kMaxBatch];
     int64_t nb;
+    int64_t skip_nb;   // > 0: segment i leaves blocks [i*skip_nb, (i+1)*skip_nb) untouched
 };
 
 struct HopArgs {
@@ -48,10 +49,13 @@ struct HopArgs {
 struct AccumArgs {
     const int8_t* q[kMaxSrc];
     const float* s[kMaxSrc];
-    uint16_t* y;
+    uint16_t* red;            // bf16 sums, segment j at j * seg_n (fused: may be null)
+    int8_t* q_out;            // fused: requantized payload, segment j at j * seg_n
+    float* s_out;             // fused: its scales, segment j at j * seg_n / 128
+    uint16_t* y[kMaxBatch];   // fused: the owner's materialization of segment j (or null)
     int nsrc;
-    int64_t nb;       // blocks per segment
-    int64_t seg_n;    // values per segment (offset of segment j is j * seg_n)
+    int64_t nb;               // blocks per segment
+    int64_t seg_n;            // values per segment
 };
 
 // Lane bookkeeping common to all INT8 kernels: the lane's block within a tile (its DPP
@@ -110,29 +114,32 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     }
 }
 
-template <int U>
+// SkipOwn: segment i leaves its own shard of blocks [i*skip_nb, (i+1)*skip_nb) untouched.
+template <int U, bool SkipOwn>
 __global__ __launch_bounds__(kGroupThreads) void k_dequant_i8(DequantArgs a) {
     const int8_t* __restrict__ q = a.q[blockIdx.y];
     const float* __restrict__ s = a.s[blockIdx.y];
     uint16_t* __restrict__ y = a.y[blockIdx.y];
     const Lanes L(U);
     const int64_t nt = tiles_of(a.nb);
+    const int64_t skip_lo = (int64_t)blockIdx.y * a.skip_nb, skip_hi = skip_lo + a.skip_nb;
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
         u32x2 qv[U];
         float sv[U];
+        bool in[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-            const bool in = b < a.nb;
-            qv[u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
-            sv[u] = in ? s[b] : 0.0f;
+            in[u] = b < a.nb && !(SkipOwn && b >= skip_lo && b < skip_hi);
+            qv[u] = in[u] ? ld8(q + b * kBlock + L.off) : u32x2{};
+            sv[u] = in[u] ? s[b] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t b = (t0 + u) * kTileBlocks + L.sub;
             float f[8];
             dequant_i8x8(qv[u], sv[u], f);
-            if (b < a.nb)
+            if (in[u])
                 st16(y + b * kBlock + L.off, pack_bf16x8(f));
         }
     }
@@ -187,11 +194,14 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
 
 // Sources are consumed in chunks of 8 whose loads are all issued before the chunk's
 // ordered additions, so up to 8 independent streams are in flight per lane.
-template <int U>
+// Fused: the owner step of the all-to-all -- the bf16 sum is requantized with the
+// block-INT8 rule into the broadcast payload, and the owner's copy is materialized
+// from that payload, all while the sum is in registers.
+template <int U, bool Fused>
 __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     const int64_t seg_off = (int64_t)blockIdx.y * a.seg_n;
     const int64_t seg_sb = seg_off / kBlock;
-    uint16_t* __restrict__ y = a.y + seg_off;
+    uint16_t* __restrict__ red = a.red ? a.red + seg_off : nullptr;
     const Lanes L(U);
     const int64_t nt = tiles_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
@@ -235,8 +245,34 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-            if (b < a.nb)
-                st16(y + b * kBlock + L.off, pack_bf16x8(acc[u]));
+            const u32x4 rb = pack_bf16x8(acc[u]);       // the owner's bf16 sum
+            if constexpr (!Fused) {
+                if (b < a.nb)
+                    st16(red + b * kBlock + L.off, rb);
+            } else {
+                float f[8];
+                unpack_bf16x8(rb, f);
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+                const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+                const float sc = i8_scale(amax);
+                const u32x2 qv = quant_i8x8(f, sc);
+                if (b < a.nb) {
+                    st8(a.q_out + seg_off + b * kBlock + L.off, qv);
+                    if (L.leader)
+                        a.s_out[seg_sb + b] = sc;
+                    if (red)
+                        st16(red + b * kBlock + L.off, rb);
+                    uint16_t* y = a.y[blockIdx.y];
+                    if (y) {
+                        float g[8];
+                        dequant_i8x8(qv, sc, g);
+                        st16(y + b * kBlock + L.off, pack_bf16x8(g));
+                    }
+                }
+            }
         }
     }
 }
@@ -271,15 +307,20 @@ hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q
 }
 
 hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
-                             uint16_t* const* y, int64_t n, hipStream_t stream) {
+                             uint16_t* const* y, int64_t n, hipStream_t stream,
+                             int64_t skip_shard_n) {
     DequantArgs a{};
+    a.skip_nb = skip_shard_n / kBlock;
     for (int i = 0; i < count; ++i) {
         a.q[i] = q[i];
         a.s[i] = s[i];
         a.y[i] = y[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_dequant_i8<kUDequant>, grid_for<kUDequant>(a.nb, count), dim3(kGroupThreads), stream, a);
+    const dim3 grid = grid_for<kUDequant>(a.nb, count);
+    if (a.skip_nb > 0)
+        return launch1(k_dequant_i8<kUDequant, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_dequant_i8<kUDequant, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
@@ -304,11 +345,32 @@ hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const*
         a.q[i] = q[i];
         a.s[i] = s[i];
     }
-    a.y = y;
+    a.red = y;
     a.nsrc = nsrc;
     a.nb = seg_n / kBlock;
     a.seg_n = seg_n;
-    return launch1(k_accum_i8<kUAccum>, grid_for<kUAccum>(a.nb, nseg), dim3(kGroupThreads), stream, a);
+    return launch1(k_accum_i8<kUAccum, false>, grid_for<kUAccum>(a.nb, nseg),
+                   dim3(kGroupThreads), stream, a);
+}
+
+hipError_t launch_a2a_reduce_i8(int nsrc, const int8_t* const* q, const float* const* s,
+                                int nseg, int64_t seg_n, int8_t* q_out, float* s_out,
+                                uint16_t* const* y, uint16_t* red, hipStream_t stream) {
+    AccumArgs a{};
+    for (int i = 0; i < nsrc; ++i) {
+        a.q[i] = q[i];
+        a.s[i] = s[i];
+    }
+    for (int j = 0; j < nseg; ++j)
+        a.y[j] = y ? y[j] : nullptr;
+    a.red = red;
+    a.q_out = q_out;
+    a.s_out = s_out;
+    a.nsrc = nsrc;
+    a.nb = seg_n / kBlock;
+    a.seg_n = seg_n;
+    return launch1(k_accum_i8<kUAccum, true>, grid_for<kUAccum>(a.nb, nseg),
+                   dim3(kGroupThreads), stream, a);
 }
 
 }  // namespace bq

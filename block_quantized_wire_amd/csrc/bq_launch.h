@@ -22,8 +22,11 @@ hipError_t launch1(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t strea
 // Block INT8.  Segment i of a batch is (x[i] -> q[i], s[i]), n values each.
 hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
                            float* const* s, int64_t n, hipStream_t stream);
+// skip_shard_n > 0: segment i leaves values [i*skip_shard_n, (i+1)*skip_shard_n) of
+// its output untouched (the shard an all-to-all owner has already materialized).
 hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
-                             uint16_t* const* y, int64_t n, hipStream_t stream);
+                             uint16_t* const* y, int64_t n, hipStream_t stream,
+                             int64_t skip_shard_n = 0);
 hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
                               const uint16_t* const* local, int8_t* const* q_out,
                               float* const* s_out, int64_t n, hipStream_t stream);
@@ -31,6 +34,12 @@ hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float*
 // every source k in order and writes y + j*seg_n.
 hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
                            uint16_t* y, int nseg, int64_t seg_n, hipStream_t stream);
+// The fused all-to-all owner step: accumulate as above, requantize each owner's bf16
+// sum into q_out/s_out (segment j at j*seg_n), materialize it into y[j] (y or y[j] may
+// be null) and store the bf16 sums into red (may be null).
+hipError_t launch_a2a_reduce_i8(int nsrc, const int8_t* const* q, const float* const* s,
+                                int nseg, int64_t seg_n, int8_t* q_out, float* s_out,
+                                uint16_t* const* y, uint16_t* red, hipStream_t stream);
 
 // MXFP8 (row-major with leading dimensions; cols a multiple of 128).
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,

@@ -90,6 +90,20 @@ bq_status bq_dequant_accum_i8_batch(int nseg, int nsrc, const int8_t* const* q_s
                                     const float* const* s_srcs, int64_t seg_n, uint16_t* y,
                                     void* stream);
 
+/* Fused all-to-all owner step, one pass, bit-identical to bq_dequant_accum_i8_batch ->
+ * bq_quant_i8 -> bq_dequant_i8 (P1 Summary and Implementation: quantize-once A2A, owner
+ * materializes from the payload it broadcasts).  Owner j (0 <= j < nseg) sums shard j --
+ * values [j*seg_n, (j+1)*seg_n) -- of the nsrc sources in binary32 in source order, rounds
+ * the sum to bf16, requantizes that bf16 sum with the bq_quant_i8 rule into q_out/s_out
+ * (segment j at value offset j*seg_n), and materializes the owner's copy from that same
+ * payload into y_out[j] (bf16[seg_n]).  red, if not NULL, receives the bf16 sums
+ * (segment j at j*seg_n).  q_srcs, s_srcs: host arrays of nsrc device pointers to
+ * nseg*seg_n values each; y_out: host array of nseg device pointers, or NULL to skip
+ * the materialization.  1 <= nseg <= BQ_MAX_BATCH, 1 <= nsrc <= BQ_MAX_SRC. */
+bq_status bq_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
+                           const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
+                           float* s_out, uint16_t* const* y_out, uint16_t* red, void* stream);
+
 /* One fused ring reduce-scatter hop: per value sum = fl32(fl32(q_in * s_in) + local) in
  * binary32, then the binary32 sums of each block are requantized with the
  * bq_quant_i8 rule (no bf16 intermediate).  q_in: int8[n]; s_in: float[n/128];
@@ -113,6 +127,15 @@ bq_status bq_ring_hop_i8_batch(int count, const int8_t* const* q_in, const float
 
 /* ==== Collectives simulated on one GPU: a "rank" is a separate HBM buffer ========== */
 
+/* INT8 all-gather materialization (P1 Summary: every rank, the owner included,
+ * materializes from the same final payload): each of `world` ranks materializes the
+ * whole shared payload q (int8[n]) / s (float[n/128]) into out[r] (bf16[n]), one launch.
+ * With skip_own != 0, rank r leaves its own shard -- values [r*n/W, (r+1)*n/W) --
+ * untouched (an owner that materialized it in the fused owner step).  out: host array of
+ * W device pointers.  n divisible by 128*world; 1 <= W <= BQ_MAX_BATCH. */
+bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, int64_t n,
+                                  uint16_t* const* out, int skip_own, void* stream);
+
 /* i8_ring all-reduce (P1 Summary): INT8 ring reduce-scatter, then INT8 all-gather of
  * the final payloads.  The n values of every rank are cut into `world` equal chunks
  * (n divisible by 128*world), chunk c owned by rank c.  Step 0: rank r quantizes its
@@ -130,12 +153,13 @@ bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* part
 
 /* i8_a2a all-reduce (P1 Summary, Implementation): every rank quantizes its partial
  * once into q_send[r]/s_send[r]; owner j dequantizes shard j of the W payloads and
- * accumulates them in binary32 in rank order into red (bf16, shard j at offset j*n/W);
- * it requantizes that bf16 sum once into q_bcast/s_bcast; every rank materializes
- * every shard from that broadcast payload into out[r].
- * partials, q_send, s_send, out: host arrays of W device pointers (bf16[n], int8[n],
- * float[n/128], bf16[n]); red: bf16[n]; q_bcast: int8[n]; s_bcast: float[n/128].
- * n divisible by 128*world; 1 <= W <= BQ_MAX_BATCH. */
+ * accumulates them in binary32 in rank order (a bf16 sum, stored into red at offset
+ * j*n/W when red is not NULL); it requantizes that bf16 sum once into q_bcast/s_bcast;
+ * every rank materializes every shard from that broadcast payload into out[r].  The
+ * owner step runs fused (bq_a2a_reduce_i8), the owner's own shard materialized in the
+ * same pass.  partials, q_send, s_send, out: host arrays of W device pointers (bf16[n],
+ * int8[n], float[n/128], bf16[n]); red: bf16[n] or NULL; q_bcast: int8[n];
+ * s_bcast: float[n/128].  n divisible by 128*world; 1 <= W <= BQ_MAX_BATCH. */
 bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
                               int8_t* const* q_send, float* const* s_send, uint16_t* red,
                               int8_t* q_bcast, float* s_bcast, uint16_t* const* out,

@@ -5,8 +5,9 @@ benchmark's CPU-baseline leg may import this package.  The GPU library never
 imports it, and it imports nothing from the GPU library.
 
 All arrays are numpy: bf16 tensors as uint16 bit patterns, INT8 payloads as
-int8, E4M3 / E8M0 bytes as uint8, scales as float32.  Functions allocate and
-return their outputs.  The C functions they wrap cite the pages they follow.
+int8, E4M3 / E8M0 bytes as uint8, scales as float32.  Functions allocate their
+outputs zero-filled (so an output a planted mistake leaves unwritten reads as
+zeros, deterministically) and return them.  The C functions they wrap cite the pages they follow.
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ _SIGS = {
     "orc_dequant_i8": ([_P, _P, _I64, _P], None),
     "orc_dequant_accum_i8": ([ctypes.c_int, _P, _P, _I64, _P], None),
     "orc_ring_hop_i8": ([_P, _P, _P, _I64, _P, _P], None),
+    "orc_a2a_reduce_i8": ([ctypes.c_int, ctypes.c_int, _P, _P, _I64, _P, _P, _P, _P], None),
     "orc_ring_allreduce_i8": ([ctypes.c_int, _I64, _P, _P, _P, _P], None),
     "orc_a2a_allreduce_i8": ([ctypes.c_int, _I64, _P, _P, _P, _P, _P], None),
     "orc_quant_mx": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
@@ -109,8 +111,8 @@ def e8m0_scale(amax: float) -> int:
 
 def quant_i8(x: np.ndarray):
     x = _c(x, np.uint16).reshape(-1)
-    q = np.empty(x.size, np.int8)
-    s = np.empty(x.size // 128, np.float32)
+    q = np.zeros(x.size, np.int8)
+    s = np.zeros(x.size // 128, np.float32)
     lib().orc_quant_i8(x.ctypes.data, x.size, q.ctypes.data, s.ctypes.data)
     return q, s
 
@@ -119,7 +121,7 @@ def dequant_i8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     q = _c(q, np.int8).reshape(-1)
     s = _c(s, np.float32).reshape(-1)
     assert s.size * 128 == q.size
-    y = np.empty(q.size, np.uint16)
+    y = np.zeros(q.size, np.uint16)
     lib().orc_dequant_i8(q.ctypes.data, s.ctypes.data, q.size, y.ctypes.data)
     return y
 
@@ -129,7 +131,7 @@ def dequant_accum_i8(qs, ss) -> np.ndarray:
     ss = [_c(s, np.float32).reshape(-1) for s in ss]
     n = qs[0].size
     assert all(q.size == n for q in qs) and all(s.size * 128 == n for s in ss)
-    y = np.empty(n, np.uint16)
+    y = np.zeros(n, np.uint16)
     lib().orc_dequant_accum_i8(len(qs), _ptrs(qs), _ptrs(ss), n, y.ctypes.data)
     return y
 
@@ -140,20 +142,36 @@ def ring_hop_i8(q_in: np.ndarray, s_in: np.ndarray, local: np.ndarray):
     local = _c(local, np.uint16).reshape(-1)
     n = q_in.size
     assert local.size == n and s_in.size * 128 == n
-    q = np.empty(n, np.int8)
-    s = np.empty(n // 128, np.float32)
+    q = np.zeros(n, np.int8)
+    s = np.zeros(n // 128, np.float32)
     lib().orc_ring_hop_i8(q_in.ctypes.data, s_in.ctypes.data, local.ctypes.data, n,
                           q.ctypes.data, s.ctypes.data)
     return q, s
+
+
+def a2a_reduce_i8(qs, ss, nseg: int):
+    """Owner step of the all-to-all for nseg owners: returns (q, s, ys, red) where segment j
+    of q/s/red is owner j's payload / scales / bf16 sum and ys[j] its materialized shard."""
+    qs = [_c(q, np.int8).reshape(-1) for q in qs]
+    ss = [_c(s, np.float32).reshape(-1) for s in ss]
+    n = qs[0].size
+    seg_n = n // nseg
+    q = np.zeros(n, np.int8)
+    s = np.zeros(n // 128, np.float32)
+    red = np.zeros(n, np.uint16)
+    ys = [np.zeros(seg_n, np.uint16) for _ in range(nseg)]
+    lib().orc_a2a_reduce_i8(nseg, len(qs), _ptrs(qs), _ptrs(ss), seg_n, q.ctypes.data,
+                            s.ctypes.data, _ptrs(ys), red.ctypes.data)
+    return q, s, ys, red
 
 
 def ring_allreduce_i8(partials):
     """Returns (q_final, s_final, outs): final payload of every chunk and each rank's bf16 output."""
     ps = [_c(p, np.uint16).reshape(-1) for p in partials]
     W, n = len(ps), ps[0].size
-    q = np.empty(n, np.int8)
-    s = np.empty(n // 128, np.float32)
-    outs = [np.empty(n, np.uint16) for _ in range(W)]
+    q = np.zeros(n, np.int8)
+    s = np.zeros(n // 128, np.float32)
+    outs = [np.zeros(n, np.uint16) for _ in range(W)]
     lib().orc_ring_allreduce_i8(W, n, _ptrs(ps), q.ctypes.data, s.ctypes.data, _ptrs(outs))
     return q, s, outs
 
@@ -162,10 +180,10 @@ def a2a_allreduce_i8(partials):
     """Returns (red, q_final, s_final, outs): owner bf16 sums, broadcast payloads, outputs."""
     ps = [_c(p, np.uint16).reshape(-1) for p in partials]
     W, n = len(ps), ps[0].size
-    red = np.empty(n, np.uint16)
-    q = np.empty(n, np.int8)
-    s = np.empty(n // 128, np.float32)
-    outs = [np.empty(n, np.uint16) for _ in range(W)]
+    red = np.zeros(n, np.uint16)
+    q = np.zeros(n, np.int8)
+    s = np.zeros(n // 128, np.float32)
+    outs = [np.zeros(n, np.uint16) for _ in range(W)]
     lib().orc_a2a_allreduce_i8(W, n, _ptrs(ps), red.ctypes.data, q.ctypes.data, s.ctypes.data,
                                _ptrs(outs))
     return red, q, s, outs
@@ -177,8 +195,8 @@ def quant_mx(x: np.ndarray):
     """x: (rows, cols) uint16 bf16 -> (values uint8 (rows, cols), e8m0 uint8 (rows, cols/32))."""
     x = _c(x, np.uint16)
     rows, cols = x.shape
-    v = np.empty((rows, cols), np.uint8)
-    e = np.empty((rows, cols // 32), np.uint8)
+    v = np.zeros((rows, cols), np.uint8)
+    e = np.zeros((rows, cols // 32), np.uint8)
     lib().orc_quant_mx(x.ctypes.data, rows, cols, cols, v.ctypes.data, cols, e.ctypes.data,
                        cols // 32)
     return v, e
@@ -189,7 +207,7 @@ def dequant_mx(v: np.ndarray, e: np.ndarray) -> np.ndarray:
     e = _c(e, np.uint8)
     rows, cols = v.shape
     assert e.shape == (rows, cols // 32)
-    y = np.empty((rows, cols), np.uint16)
+    y = np.zeros((rows, cols), np.uint16)
     lib().orc_dequant_mx(v.ctypes.data, cols, e.ctypes.data, cols // 32, rows, cols,
                          y.ctypes.data, cols)
     return y
@@ -211,8 +229,8 @@ def quant_mx_slice(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray) ->
 
 def quant_e4m3_b128(x: np.ndarray):
     x = _c(x, np.uint16).reshape(-1)
-    v = np.empty(x.size, np.uint8)
-    s = np.empty(x.size // 128, np.float32)
+    v = np.zeros(x.size, np.uint8)
+    s = np.zeros(x.size // 128, np.float32)
     lib().orc_quant_e4m3_b128(x.ctypes.data, x.size, v.ctypes.data, s.ctypes.data)
     return v, s
 
@@ -221,6 +239,6 @@ def dequant_e4m3_b128(v: np.ndarray, s: np.ndarray) -> np.ndarray:
     v = _c(v, np.uint8).reshape(-1)
     s = _c(s, np.float32).reshape(-1)
     assert s.size * 128 == v.size
-    y = np.empty(v.size, np.uint16)
+    y = np.zeros(v.size, np.uint16)
     lib().orc_dequant_e4m3_b128(v.ctypes.data, s.ctypes.data, v.size, y.ctypes.data)
     return y

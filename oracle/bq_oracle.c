@@ -223,6 +223,39 @@ void orc_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* loca
     }
 }
 
+/* The owner step of the quantize-once all-to-all (P1 Summary and Implementation):
+ * accumulate the sources' shard in binary32 (bf16 result), requantize that bf16 sum
+ * once, and materialize the owner's copy from the payload it broadcasts.  Written as
+ * the composition of the three steps above, which is the definition. */
+void orc_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
+                       const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
+                       float* s_out, uint16_t* const* y_out, uint16_t* red) {
+    need_blocks(seg_n);
+    const int8_t** qp = (const int8_t**)malloc((size_t)nsrc * sizeof(*qp));
+    const float** sp = (const float**)malloc((size_t)nsrc * sizeof(*sp));
+    uint16_t* sum = (uint16_t*)malloc((size_t)(seg_n ? seg_n : 1) * sizeof(uint16_t));
+    if (!qp || !sp || !sum) {
+        fprintf(stderr, "bq_oracle: out of memory\n");
+        abort();
+    }
+    int64_t sb = seg_n / BLK;
+    for (int j = 0; j < nseg; j++) {
+        for (int k = 0; k < nsrc; k++) {
+            qp[k] = q_srcs[k] + j * seg_n;
+            sp[k] = s_srcs[k] + j * sb;
+        }
+        orc_dequant_accum_i8(nsrc, qp, sp, seg_n, sum);
+        orc_quant_i8(sum, seg_n, q_out + j * seg_n, s_out + j * sb);
+        if (y_out && y_out[j])
+            orc_dequant_i8(q_out + j * seg_n, s_out + j * sb, seg_n, y_out[j]);
+        if (red)
+            memcpy(red + j * seg_n, sum, (size_t)seg_n * sizeof(uint16_t));
+    }
+    free(qp);
+    free(sp);
+    free(sum);
+}
+
 /* ---------------------------------------------------------------------- */
 /* Collectives simulated on one host: a "rank" is only a separate buffer.   */
 /* ---------------------------------------------------------------------- */

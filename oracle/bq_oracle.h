@@ -48,6 +48,15 @@ void orc_dequant_accum_i8(int nsrc, const int8_t* const* q, const float* const* 
 void orc_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* local,
                      int64_t n, int8_t* q_out, float* s_out);
 
+/* Fused all-to-all owner step: for each of nseg owners, the accumulate above over
+ * values [j*seg_n, (j+1)*seg_n) of every source, its bf16 sum requantized with the
+ * block-INT8 rule into q_out/s_out (segment j at j*seg_n), and the owner's own
+ * materialization of that payload into y_out[j] (may be NULL); red (may be NULL)
+ * receives the bf16 sums. */
+void orc_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
+                       const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
+                       float* s_out, uint16_t* const* y_out, uint16_t* red);
+
 /* ---- one-GPU simulation of the collectives (P1 Summary) --------------- */
 /* Ring reduce-scatter + all-gather of `world` rank partials of n values each.
  * q_final/s_final receive the final payload of every chunk, chunk c at value

@@ -150,6 +150,32 @@ def test_collective_driver_errors():
     assert L.bq_a2a_allreduce_i8(0, n, parts, qsend, ssend, red, qb, sb, outs, S) == NSRC
 
 
+def test_a2a_reduce_and_allgather_errors():
+    n = 1024
+    qs = arr(A, A + 4096)
+    ss = arr(A + 8192, A + 8192 + 64)
+    qo, so, red = A + 65536, A + 65536 + 8192, A + 65536 + 16384
+    ys = arr(A + 2 ** 20, A + 2 ** 20 + 4096)
+    f = L.bq_a2a_reduce_i8
+    assert f(0, 2, qs, ss, n, qo, so, ys, red, S) == NSRC
+    assert f(2, 0, qs, ss, n, qo, so, ys, red, S) == NSRC
+    assert f(2, 65, qs, ss, n, qo, so, ys, red, S) == NSRC
+    assert f(2, 2, qs, ss, 100, qo, so, ys, red, S) == SIZE
+    assert f(2, 2, None, ss, n, qo, so, ys, red, S) == NULL
+    assert f(2, 2, qs, ss, n, None, so, ys, red, S) == NULL
+    assert f(2, 2, qs, ss, n, A + 16, so, ys, red, S) == ALIAS        # q_out over a source
+    assert f(2, 2, qs, ss, n, qo, so, arr(A + 2 ** 20, A + 2 ** 20 + 1024), red, S) == ALIAS
+    assert f(2, 2, qs, ss, n, qo, so, ys, qo + 64, S) == ALIAS        # red over q_out
+    assert f(2, 2, qs, ss, n, qo, so, arr(A + 2 ** 20 + 8, A + 2 ** 21), None, S) == ALIGN
+    g = L.bq_allgather_dequant_i8
+    outs = arr(A + 2 ** 22, A + 2 ** 22 + 8192)
+    assert g(0, A, A + 4096, n, outs, 1, S) == NSRC
+    assert g(2, A, A + 4096, 128 * 3, outs, 1, S) == SIZE
+    assert g(2, A, A + 4096, n, arr(A + 2 ** 22, A + 2 ** 22 + 1024), 1, S) == ALIAS
+    assert g(2, A, A + 4096, n, arr(A + 2 ** 22, A + 512), 0, S) == ALIAS
+    assert g(2, None, A + 4096, n, outs, 1, S) == NULL
+
+
 def test_mx_errors():
     rows, cols = 16, 512
     x, v, e = A, A + 2 ** 20, A + 2 ** 21

@@ -326,6 +326,70 @@ def test_a2a_cfg3_w16_sampled():
     assert_same(host(outs[0], np.uint16).reshape(R, COLS)[rows].reshape(-1), wouts[0], "output")
 
 
+@pytest.mark.parametrize("nseg,nsrc,rows", [(4, 4, 48), (2, 3, 6), (16, 16, 32), (1, 1, 3)])
+def test_a2a_reduce_fused_matches_oracle(nseg, nsrc, rows):
+    say(f"fused a2a owner step nseg={nseg} nsrc={nsrc} rows={rows}")
+    parts = [workloads.rows(3, r, 0, rows, 1024).reshape(-1) for r in range(nsrc)]
+    qs, ss = zip(*[oracle.quant_i8(p) for p in parts])
+    wq, ws, wys, wred = oracle.a2a_reduce_i8(list(qs), list(ss), nseg)
+    n = parts[0].size
+    m = n // nseg
+    qd, sd = [to_dev(q) for q in qs], [to_dev(v) for v in ss]
+    qo, so, red = empty(n, np.int8), empty(n // 128, np.float32), empty(n, np.uint16)
+    ys = [empty(m, np.uint16) for _ in range(nseg)]
+    bq.bq_a2a_reduce_i8(nseg, qd, sd, qo, so, ys, red)
+    qo2, so2 = empty(n, np.int8), empty(n // 128, np.float32)
+    bq.bq_a2a_reduce_i8(nseg, qd, sd, qo2, so2)          # payload only
+    sync()
+    assert_same(host(qo, np.int8), wq, "payload")
+    assert_same(host(so, np.float32), ws, "scales")
+    assert_same(host(red, np.uint16), wred, "bf16 sums")
+    for j in range(nseg):
+        assert_same(host(ys[j], np.uint16), wys[j], f"owner {j} materialization")
+    assert_same(host(qo2, np.int8), wq, "payload without optional outputs")
+    assert_same(host(so2, np.float32), ws, "scales without optional outputs")
+
+
+def test_allgather_dequant_skip_own_leaves_the_owner_shard():
+    say("all-gather materialization with and without skip_own")
+    W, rows = 4, 16
+    x = workloads.rows(6, 0, 0, rows, COLS).reshape(-1)
+    q, s = oracle.quant_i8(x)
+    want = oracle.dequant_i8(q, s)
+    n, m = x.size, x.size // W
+    qd, sd = to_dev(q), to_dev(s)
+    outs = [filled(n, np.uint16, 0x7B) for _ in range(W)]
+    bq.bq_allgather_dequant_i8(qd, sd, outs, skip_own=True)
+    full = [empty(n, np.uint16) for _ in range(W)]
+    bq.bq_allgather_dequant_i8(qd, sd, full)
+    sync()
+    for r in range(W):
+        got = host(outs[r], np.uint16)
+        own = np.zeros(n, bool)
+        own[r * m:(r + 1) * m] = True
+        assert np.all(got[own] == 0x7B7B), f"rank {r} own shard was written"
+        assert_same(got[~own], want[~own], f"rank {r} other shards")
+        assert_same(host(full[r], np.uint16), want, f"rank {r} full")
+
+
+def test_a2a_driver_without_red():
+    say("a2a driver, red = NULL")
+    W = 4
+    parts = [workloads.rows(3, r, 0, 96, COLS).reshape(-1) for r in range(W)]
+    wred, wq, ws, wouts = oracle.a2a_allreduce_i8(parts)
+    n = parts[0].size
+    pd = [to_dev(p) for p in parts]
+    qs = [empty(n, np.int8) for _ in range(W)]
+    ss = [empty(n // 128, np.float32) for _ in range(W)]
+    qb, sb = empty(n, np.int8), empty(n // 128, np.float32)
+    outs = [empty(n, np.uint16) for _ in range(W)]
+    bq.bq_a2a_allreduce_i8(pd, qs, ss, None, qb, sb, outs, n=n)
+    sync()
+    assert_same(host(qb, np.int8), wq, "payload")
+    for r in range(W):
+        assert_same(host(outs[r], np.uint16), wouts[r], f"rank {r} output")
+
+
 # ---- MXFP8 ---------------------------------------------------------------------------------
 
 def gpu_quant_mx(x: np.ndarray, ldv_pad: int = 0, lds_pad: int = 0):

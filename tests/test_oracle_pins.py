@@ -556,3 +556,25 @@ def test_layout_figures_from_the_pages():
     assert x.nbytes // (n // 128) == int(kv["bytes_per_128_bf16"])
     cut = 100.0 * (1 - int(kv["bytes_per_block_i8"]) / int(kv["bytes_per_128_bf16"]))
     assert round(cut, 1) == float(kv["wire_reduction_percent_1dp"])
+
+
+def test_a2a_reduce_is_accumulate_then_quantize_then_materialize():
+    """The fused owner step is, by definition, A3 -> A1 -> A2 on each owner's shard;
+    pinned against the separately pinned steps and against the all-to-all driver."""
+    W = 4
+    parts = [workloads.rows(3, r, 0, 8, 1024).reshape(-1) for r in range(W)]
+    qs, ss = zip(*[oracle.quant_i8(p) for p in parts])
+    q, s, ys, red = oracle.a2a_reduce_i8(list(qs), list(ss), W)
+    m = parts[0].size // W
+    for j in range(W):
+        sm = oracle.dequant_accum_i8([qq[j * m:(j + 1) * m] for qq in qs],
+                                     [sv[j * m // 128:(j + 1) * m // 128] for sv in ss])
+        assert np.array_equal(red[j * m:(j + 1) * m], sm)
+        wq, ws = oracle.quant_i8(sm)
+        assert np.array_equal(q[j * m:(j + 1) * m], wq)
+        assert np.array_equal(s[j * m // 128:(j + 1) * m // 128], ws)
+        assert np.array_equal(ys[j], oracle.dequant_i8(wq, ws))
+    dred, dq, ds, douts = oracle.a2a_allreduce_i8(parts)
+    assert np.array_equal(dred, red) and np.array_equal(dq, q) and np.array_equal(ds, s)
+    for j in range(W):
+        assert np.array_equal(douts[j][j * m:(j + 1) * m], ys[j])
