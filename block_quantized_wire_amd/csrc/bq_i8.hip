@@ -61,20 +61,27 @@ struct AccumArgs {
 // Lane bookkeeping common to all INT8 kernels: the lane's block within a tile (its DPP
 // row) and its first value in that block.  Waves walk the tiles grid-stride, U adjacent
 // tiles per step, so a launch needs no more workgroups than the chip holds at once.
+// The wave index is read from the first lane, so the tile a wave works on is a uniform
+// (scalar) value: each access is a scalar base of the step plus a small 32-bit lane
+// offset, which keeps addresses out of the vector registers.
 struct Lanes {
-    int sub, off;
+    uint32_t sub, off;
     bool leader;     // first lane of the row: stores the block's scale
     int64_t first;   // first tile of this wave
     int64_t step;    // tiles between successive steps of this wave
     __device__ explicit Lanes(int U) {
-        const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
+        const uint32_t lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         sub = lane >> 4;
         off = (lane & 15) * kLaneVals;
         leader = (lane & 15) == 0;
         first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
         step = (int64_t)gridDim.x * kWavesPerGroup * U;
     }
+    // block of tile u of a step, counted from the step's first block
+    __device__ __forceinline__ uint32_t blk(int u) const { return (uint32_t)u * kTileBlocks + sub; }
+    // first value of this lane in tile u of a step, counted from the step's first value
+    __device__ __forceinline__ uint32_t val(int u) const { return blk(u) * kBlock + off; }
 };
 
 __device__ __forceinline__ int64_t tiles_of(int64_t nb) { return (nb + kTileBlocks - 1) / kTileBlocks; }
@@ -87,15 +94,13 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     const Lanes L(U);
     const int64_t nt = tiles_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
         u32x4 xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-            xv[u] = (b < a.nb) ? ld16(x + b * kBlock + L.off) : u32x4{};
-        }
+        for (int u = 0; u < U; ++u)
+            xv[u] = (L.blk(u) < left) ? ld16(x + b0 * kBlock + L.val(u)) : u32x4{};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
             float f[8];
             unpack_bf16x8(xv[u], f);
             float m = 0.0f;
@@ -105,10 +110,10 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
             const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
             const float sc = i8_scale(amax);
             const u32x2 qv = quant_i8x8(f, sc);
-            if (b < a.nb) {
-                st8(q + b * kBlock + L.off, qv);
+            if (L.blk(u) < left) {
+                st8(q + b0 * kBlock + L.val(u), qv);
                 if (L.leader)
-                    s[b] = sc;
+                    s[b0 + L.blk(u)] = sc;
             }
         }
     }
@@ -124,23 +129,23 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_i8(DequantArgs a) {
     const int64_t nt = tiles_of(a.nb);
     const int64_t skip_lo = (int64_t)blockIdx.y * a.skip_nb, skip_hi = skip_lo + a.skip_nb;
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
         u32x2 qv[U];
         float sv[U];
         bool in[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-            in[u] = b < a.nb && !(SkipOwn && b >= skip_lo && b < skip_hi);
-            qv[u] = in[u] ? ld8(q + b * kBlock + L.off) : u32x2{};
-            sv[u] = in[u] ? s[b] : 0.0f;
+            const int64_t r = L.blk(u);
+            in[u] = r < left && !(SkipOwn && r >= skip_lo - b0 && r < skip_hi - b0);
+            qv[u] = in[u] ? ld8(q + b0 * kBlock + L.val(u)) : u32x2{};
+            sv[u] = in[u] ? s[b0 + L.blk(u)] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
             float f[8];
             dequant_i8x8(qv[u], sv[u], f);
             if (in[u])
-                st16(y + b * kBlock + L.off, pack_bf16x8(f));
+                st16(y + b0 * kBlock + L.val(u), pack_bf16x8(f));
         }
     }
 }
@@ -157,20 +162,19 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
     const Lanes L(U);
     const int64_t nt = tiles_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
         u32x2 qv[U];
         u32x4 lv[U];
         float sv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-            const bool in = b < a.nb;
-            qv[u] = in ? ld8(q_in + b * kBlock + L.off) : u32x2{};
-            sv[u] = in ? s_in[b] : 0.0f;
-            lv[u] = in ? ld16(local + b * kBlock + L.off) : u32x4{};
+            const bool in = L.blk(u) < left;
+            qv[u] = in ? ld8(q_in + b0 * kBlock + L.val(u)) : u32x2{};
+            sv[u] = in ? s_in[b0 + L.blk(u)] : 0.0f;
+            lv[u] = in ? ld16(local + b0 * kBlock + L.val(u)) : u32x4{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
             float deq[8], loc[8], sum[8];
             dequant_i8x8(qv[u], sv[u], deq);        // rounded products ...
             unpack_bf16x8(lv[u], loc);
@@ -183,20 +187,21 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
             const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
             const float sc = i8_scale(amax);
             const u32x2 out = quant_i8x8(sum, sc);
-            if (b < a.nb) {
-                st8(q_out + b * kBlock + L.off, out);
+            if (L.blk(u) < left) {
+                st8(q_out + b0 * kBlock + L.val(u), out);
                 if (L.leader)
-                    s_out[b] = sc;
+                    s_out[b0 + L.blk(u)] = sc;
             }
         }
     }
 }
 
-// Sources are consumed in chunks of 8 whose loads are all issued before the chunk's
-// ordered additions, so up to 8 independent streams are in flight per lane.
+// Sources are consumed in chunks of kSrcChunk whose loads are all issued before the
+// chunk's ordered additions, so that many independent streams are in flight per lane.
 // Fused: the owner step of the all-to-all -- the bf16 sum is requantized with the
 // block-INT8 rule into the broadcast payload, and the owner's copy is materialized
 // from that payload, all while the sum is in registers.
+constexpr int kSrcChunk = 4;
 template <int U, bool Fused>
 __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     const int64_t seg_off = (int64_t)blockIdx.y * a.seg_n;
@@ -205,31 +210,32 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     const Lanes L(U);
     const int64_t nt = tiles_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
+        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
+        const int64_t v0 = seg_off + b0 * kBlock, sb0 = seg_sb + b0;
         float acc[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 acc[u][i] = 0.0f;
-        for (int k0 = 0; k0 < a.nsrc; k0 += 8) {
-            u32x2 qv[8][U];
-            float sv[8][U];
+        for (int k0 = 0; k0 < a.nsrc; k0 += kSrcChunk) {
+            u32x2 qv[kSrcChunk][U];
+            float sv[kSrcChunk][U];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kSrcChunk; ++j) {
                 if (k0 + j < a.nsrc) {
-                    const int8_t* q = a.q[k0 + j] + seg_off;
-                    const float* s = a.s[k0 + j] + seg_sb;
+                    const int8_t* q = a.q[k0 + j] + v0;
+                    const float* s = a.s[k0 + j] + sb0;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const int64_t b = (t0 + u) * kTileBlocks + L.sub;
-                        const bool in = b < a.nb;
-                        qv[j][u] = in ? ld8(q + b * kBlock + L.off) : u32x2{};
-                        sv[j][u] = in ? s[b] : 0.0f;
+                        const bool in = L.blk(u) < left;
+                        qv[j][u] = in ? ld8(q + L.val(u)) : u32x2{};
+                        sv[j][u] = in ? s[L.blk(u)] : 0.0f;
                     }
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kSrcChunk; ++j) {
                 if (k0 + j < a.nsrc) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -244,11 +250,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + L.sub;
+            const bool in = L.blk(u) < left;
             const u32x4 rb = pack_bf16x8(acc[u]);       // the owner's bf16 sum
             if constexpr (!Fused) {
-                if (b < a.nb)
-                    st16(red + b * kBlock + L.off, rb);
+                if (in)
+                    st16(red + b0 * kBlock + L.val(u), rb);
             } else {
                 float f[8];
                 unpack_bf16x8(rb, f);
@@ -259,17 +265,17 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
                 const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
                 const float sc = i8_scale(amax);
                 const u32x2 qv = quant_i8x8(f, sc);
-                if (b < a.nb) {
-                    st8(a.q_out + seg_off + b * kBlock + L.off, qv);
+                if (in) {
+                    st8(a.q_out + v0 + L.val(u), qv);
                     if (L.leader)
-                        a.s_out[seg_sb + b] = sc;
+                        a.s_out[sb0 + L.blk(u)] = sc;
                     if (red)
-                        st16(red + b * kBlock + L.off, rb);
+                        st16(red + b0 * kBlock + L.val(u), rb);
                     uint16_t* y = a.y[blockIdx.y];
                     if (y) {
                         float g[8];
                         dequant_i8x8(qv, sc, g);
-                        st16(y + b * kBlock + L.off, pack_bf16x8(g));
+                        st16(y + b0 * kBlock + L.val(u), pack_bf16x8(g));
                     }
                 }
             }

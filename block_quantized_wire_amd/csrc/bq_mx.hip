@@ -69,7 +69,7 @@ struct Walk {
     int64_t first, step;
     __device__ explicit Walk(int U) {
         const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // uniform
         sub = lane >> 4;
         off = (lane & 15) * kLaneVals;
         first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
