@@ -52,6 +52,11 @@ _SIGS = {
     "orc_quant_mx": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
     "orc_dequant_mx": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64], None),
     "orc_quant_mx_slice": ([_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
+    "orc_ring_hop_mx": ([_P, _P, _P, _I64, _P, _P], None),
+    "orc_dequant_accum_mx": ([ctypes.c_int, _P, _P, _I64, _P], None),
+    "orc_a2a_reduce_mx": ([ctypes.c_int, ctypes.c_int, _P, _P, _I64, _P, _P, _P, _P], None),
+    "orc_ring_allreduce_mx": ([ctypes.c_int, _I64, _P, _P, _P, _P], None),
+    "orc_a2a_allreduce_mx": ([ctypes.c_int, _I64, _P, _P, _P, _P, _P], None),
     "orc_quant_e4m3_b128": ([_P, _I64, _P, _P], None),
     "orc_dequant_e4m3_b128": ([_P, _P, _I64, _P], None),
 }
@@ -223,6 +228,82 @@ def quant_mx_slice(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray) ->
     assert e.shape[1] * 32 >= v.shape[1] and e.shape[0] == v.shape[0]
     lib().orc_quant_mx_slice(x.ctypes.data, rows, cols, cols, col_off, v.ctypes.data,
                              v.shape[1], e.ctypes.data, e.shape[1])
+
+
+# ---- MXFP8 on the collective topologies (flat: n E4M3 bytes, n/32 E8M0 bytes) ----
+
+def quant_mx_flat(x: np.ndarray):
+    x = _c(x, np.uint16).reshape(1, -1)
+    v, e = quant_mx(x)
+    return v.reshape(-1), e.reshape(-1)
+
+
+def dequant_mx_flat(v: np.ndarray, e: np.ndarray) -> np.ndarray:
+    v = _c(v, np.uint8).reshape(1, -1)
+    e = _c(e, np.uint8).reshape(1, -1)
+    return dequant_mx(v, e).reshape(-1)
+
+
+def ring_hop_mx(v_in: np.ndarray, e_in: np.ndarray, local: np.ndarray):
+    v_in = _c(v_in, np.uint8).reshape(-1)
+    e_in = _c(e_in, np.uint8).reshape(-1)
+    local = _c(local, np.uint16).reshape(-1)
+    n = v_in.size
+    assert local.size == n and e_in.size * 32 == n
+    v = np.zeros(n, np.uint8)
+    e = np.zeros(n // 32, np.uint8)
+    lib().orc_ring_hop_mx(v_in.ctypes.data, e_in.ctypes.data, local.ctypes.data, n,
+                          v.ctypes.data, e.ctypes.data)
+    return v, e
+
+
+def dequant_accum_mx(vs, es) -> np.ndarray:
+    vs = [_c(v, np.uint8).reshape(-1) for v in vs]
+    es = [_c(e, np.uint8).reshape(-1) for e in es]
+    n = vs[0].size
+    assert all(v.size == n for v in vs) and all(e.size * 32 == n for e in es)
+    y = np.zeros(n, np.uint16)
+    lib().orc_dequant_accum_mx(len(vs), _ptrs(vs), _ptrs(es), n, y.ctypes.data)
+    return y
+
+
+def a2a_reduce_mx(vs, es, nseg: int):
+    """MX owner step for nseg owners: returns (v, e, ys, red) as a2a_reduce_i8 does."""
+    vs = [_c(v, np.uint8).reshape(-1) for v in vs]
+    es = [_c(e, np.uint8).reshape(-1) for e in es]
+    n = vs[0].size
+    seg_n = n // nseg
+    v = np.zeros(n, np.uint8)
+    e = np.zeros(n // 32, np.uint8)
+    red = np.zeros(n, np.uint16)
+    ys = [np.zeros(seg_n, np.uint16) for _ in range(nseg)]
+    lib().orc_a2a_reduce_mx(nseg, len(vs), _ptrs(vs), _ptrs(es), seg_n, v.ctypes.data,
+                            e.ctypes.data, _ptrs(ys), red.ctypes.data)
+    return v, e, ys, red
+
+
+def ring_allreduce_mx(partials):
+    """Returns (v_final, e_final, outs)."""
+    ps = [_c(p, np.uint16).reshape(-1) for p in partials]
+    W, n = len(ps), ps[0].size
+    v = np.zeros(n, np.uint8)
+    e = np.zeros(n // 32, np.uint8)
+    outs = [np.zeros(n, np.uint16) for _ in range(W)]
+    lib().orc_ring_allreduce_mx(W, n, _ptrs(ps), v.ctypes.data, e.ctypes.data, _ptrs(outs))
+    return v, e, outs
+
+
+def a2a_allreduce_mx(partials):
+    """Returns (red, v_final, e_final, outs)."""
+    ps = [_c(p, np.uint16).reshape(-1) for p in partials]
+    W, n = len(ps), ps[0].size
+    red = np.zeros(n, np.uint16)
+    v = np.zeros(n, np.uint8)
+    e = np.zeros(n // 32, np.uint8)
+    outs = [np.zeros(n, np.uint16) for _ in range(W)]
+    lib().orc_a2a_allreduce_mx(W, n, _ptrs(ps), red.ctypes.data, v.ctypes.data, e.ctypes.data,
+                               _ptrs(outs))
+    return red, v, e, outs
 
 
 # ---- E4M3 128-block codec ----------------------------------------------------

@@ -123,6 +123,8 @@ uint8_t orc_e8m0_scale(float amax) {
     if (amax == 0.0f)
         return 127;
     float d = amax / E4M3_MAX;
+    if (d == 0.0f)               /* the quotient underflowed: saturate to the smallest */
+        return 0;                /* finite E8M0 value, 2^-127                           */
     int k;
     float f = frexpf(d, &k);     /* d = f * 2^k, f in [0.5, 1) */
     int e = (f == 0.5f) ? k - 1 : k;
@@ -349,28 +351,45 @@ void orc_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
 /* [32g, 32g+32) of row r.                                                  */
 /* ---------------------------------------------------------------------- */
 
+/* One group of 32 binary32 values -> its scale byte and 32 E4M3 codes: the byte from
+ * the group amax by the rule above, each value scaled by 2^-(byte-127) (ldexpf, exact
+ * wherever the result is normal; below that the E4M3 code is a signed zero either way)
+ * and encoded to E4M3FN. */
+static void quant_group_mx(const float* x, uint8_t* v, uint8_t* byte_out) {
+    float amax = 0.0f;
+    for (int i = 0; i < MXG; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    uint8_t byte = orc_e8m0_scale(amax);
+    *byte_out = byte;
+    int e = (int)byte - 127;
+    for (int i = 0; i < MXG; i++) {
+        float scaled = ldexpf(x[i], -e);
+        v[i] = orc_e4m3_encode(scaled);
+    }
+}
+
+/* e4m3 * 2^(byte-127) in binary32 (exact for every code and byte whose product is
+ * finite: E4M3 values are multiples of 2^-9 with 4 significant bits). */
+static float mx_value(uint8_t code, uint8_t byte) {
+    return ldexpf(orc_e4m3_decode(code), (int)byte - 127);
+}
+
 void orc_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                   uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds) {
     if (cols % MXG != 0) {
         fprintf(stderr, "bq_oracle: MX cols must be a multiple of 32\n");
         abort();
     }
+    float xf[MXG];
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t g = 0; g < cols / MXG; g++) {
             const uint16_t* xg = x + r * ldx + g * MXG;
-            float amax = 0.0f;
-            for (int i = 0; i < MXG; i++) {
-                float a = fabsf(orc_bf16_to_f32(xg[i]));
-                if (a > amax)
-                    amax = a;
-            }
-            uint8_t byte = orc_e8m0_scale(amax);
-            e8m0[r * lds + g] = byte;
-            int e = (int)byte - 127;
-            for (int i = 0; i < MXG; i++) {
-                float scaled = ldexpf(orc_bf16_to_f32(xg[i]), -e);
-                v[r * ldv + g * MXG + i] = orc_e4m3_encode(scaled);
-            }
+            for (int i = 0; i < MXG; i++)
+                xf[i] = orc_bf16_to_f32(xg[i]);
+            quant_group_mx(xf, v + r * ldv + g * MXG, e8m0 + r * lds + g);
         }
     }
 }
@@ -380,8 +399,7 @@ void orc_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t 
                     int64_t rows, int64_t cols, uint16_t* y, int64_t ldy) {
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t c = 0; c < cols; c++) {
-            int e = (int)e8m0[r * lds + c / MXG] - 127;
-            float val = ldexpf(orc_e4m3_decode(v[r * ldv + c]), e);
+            float val = mx_value(v[r * ldv + c], e8m0[r * lds + c / MXG]);
             y[r * ldy + c] = orc_f32_to_bf16(val);
         }
     }
@@ -400,6 +418,146 @@ void orc_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
         abort();
     }
     orc_quant_mx(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / MXG, lds);
+}
+
+/* ---------------------------------------------------------------------- */
+/* MXFP8 on the collective topologies (P2 PR body Summary / Modes: mx_ring  */
+/* and mx_a2a carry the same 132-byte-per-128 payload over the ring and the */
+/* all-to-all, with the INT8 modes' canonical-payload rule).  The tensor is */
+/* flat: n E4M3 bytes and n/32 E8M0 bytes, group g = values [32g, 32g+32). */
+/* ---------------------------------------------------------------------- */
+
+static void quant_mx_flat(const uint16_t* x, int64_t n, uint8_t* v, uint8_t* e8m0) {
+    orc_quant_mx(x, 1, n, n, v, n, e8m0, n / MXG);
+}
+
+static void dequant_mx_flat(const uint8_t* v, const uint8_t* e8m0, int64_t n, uint16_t* y) {
+    orc_dequant_mx(v, n, e8m0, n / MXG, 1, n, y, n);
+}
+
+/* One mx_ring hop: per value the binary32 sum fl32(dequantized payload value +
+ * local), then each group's 32 binary32 sums requantized with the MXFP8 rule (no
+ * bf16 intermediate, as in the INT8 hop).  v_out/e_out may equal v_in/e_in. */
+void orc_ring_hop_mx(const uint8_t* v_in, const uint8_t* e_in, const uint16_t* local,
+                     int64_t n, uint8_t* v_out, uint8_t* e_out) {
+    need_blocks(n);
+    float sums[MXG];
+    for (int64_t g = 0; g < n / MXG; g++) {
+        for (int i = 0; i < MXG; i++) {
+            float dq = mx_value(v_in[g * MXG + i], e_in[g]);
+            float lp = orc_bf16_to_f32(local[g * MXG + i]);
+            sums[i] = dq + lp;
+        }
+        quant_group_mx(sums, v_out + g * MXG, e_out + g);
+    }
+}
+
+/* The mx_a2a owner accumulate: acc = +0, then acc = acc + (source value) for the
+ * sources in array order, in binary32; y = bf16(acc). */
+void orc_dequant_accum_mx(int nsrc, const uint8_t* const* v, const uint8_t* const* e8m0,
+                          int64_t n, uint16_t* y) {
+    need_blocks(n);
+    for (int64_t i = 0; i < n; i++) {
+        float total = 0.0f;
+        for (int src = 0; src < nsrc; ++src) {
+            float term = mx_value(v[src][i], e8m0[src][i / MXG]);
+            total = total + term;
+        }
+        y[i] = orc_f32_to_bf16(total);
+    }
+}
+
+/* The mx_a2a owner step for nseg owners: the accumulate above on each owner's shard,
+ * the bf16 sum requantized with the MXFP8 rule into v_out/e_out, and the owner's copy
+ * materialized from that payload (composition of the steps, which is the definition). */
+void orc_a2a_reduce_mx(int nseg, int nsrc, const uint8_t* const* v_srcs,
+                       const uint8_t* const* e_srcs, int64_t seg_n, uint8_t* v_out,
+                       uint8_t* e_out, uint16_t* const* y_out, uint16_t* red) {
+    need_blocks(seg_n);
+    const uint8_t** vp = (const uint8_t**)xmalloc((size_t)nsrc * sizeof(*vp));
+    const uint8_t** ep = (const uint8_t**)xmalloc((size_t)nsrc * sizeof(*ep));
+    uint16_t* sum = (uint16_t*)xmalloc((size_t)seg_n * sizeof(uint16_t));
+    int64_t sg = seg_n / MXG;
+    for (int j = 0; j < nseg; j++) {
+        for (int k = 0; k < nsrc; k++) {
+            vp[k] = v_srcs[k] + j * seg_n;
+            ep[k] = e_srcs[k] + j * sg;
+        }
+        orc_dequant_accum_mx(nsrc, vp, ep, seg_n, sum);
+        quant_mx_flat(sum, seg_n, v_out + j * seg_n, e_out + j * sg);
+        if (y_out && y_out[j])
+            dequant_mx_flat(v_out + j * seg_n, e_out + j * sg, seg_n, y_out[j]);
+        if (red)
+            memcpy(red + j * seg_n, sum, (size_t)seg_n * sizeof(uint16_t));
+    }
+    free(vp);
+    free(ep);
+    free(sum);
+}
+
+/* mx_ring: the i8_ring schedule with the MXFP8 codec -- chunk c = values
+ * [c*n/W, (c+1)*n/W), quantized at step 0 by rank c+1, folded in by one hop per
+ * later step at ranks c+2, ..., c, then materialized by every rank from its final
+ * payload. */
+void orc_ring_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                           uint8_t* v_final, uint8_t* e_final, uint16_t* const* out) {
+    int W = world;
+    need_blocks(n);
+    if (W < 1 || n % ((int64_t)BLK * W) != 0) {
+        fprintf(stderr, "bq_oracle: ring needs n divisible by 128*world\n");
+        abort();
+    }
+    int64_t m = n / W, mg = m / MXG;
+    for (int r = 0; r < W; r++) {
+        int c = mod(r - 1, W);
+        quant_mx_flat(partials[r] + c * m, m, v_final + c * m, e_final + c * mg);
+    }
+    for (int k = 1; k < W; k++) {
+        for (int r = 0; r < W; r++) {
+            int chunk = mod(r - 1 - k, W);
+            orc_ring_hop_mx(v_final + chunk * m, e_final + chunk * mg, partials[r] + chunk * m,
+                            m, v_final + chunk * m, e_final + chunk * mg);
+        }
+    }
+    for (int r = 0; r < W; r++)
+        for (int c = 0; c < W; c++)
+            dequant_mx_flat(v_final + c * m, e_final + c * mg, m, out[r] + c * m);
+}
+
+/* mx_a2a: every rank quantizes its partial once with the MXFP8 rule; owner j
+ * accumulates shard j of the W payloads in rank order (bf16 sum into red), requantizes
+ * that bf16 sum once and broadcasts it; every rank materializes from the broadcast. */
+void orc_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                          uint16_t* red, uint8_t* v_final, uint8_t* e_final,
+                          uint16_t* const* out) {
+    int W = world;
+    need_blocks(n);
+    if (W < 1 || n % ((int64_t)BLK * W) != 0) {
+        fprintf(stderr, "bq_oracle: a2a needs n divisible by 128*world\n");
+        abort();
+    }
+    int64_t m = n / W, mg = m / MXG, ng = n / MXG;
+    uint8_t* vs = (uint8_t*)xmalloc((size_t)W * (size_t)n);
+    uint8_t* es = (uint8_t*)xmalloc((size_t)W * (size_t)ng);
+    const uint8_t** vp = (const uint8_t**)xmalloc((size_t)W * sizeof(*vp));
+    const uint8_t** ep = (const uint8_t**)xmalloc((size_t)W * sizeof(*ep));
+    for (int r = 0; r < W; r++)
+        quant_mx_flat(partials[r], n, vs + (size_t)r * n, es + (size_t)r * ng);
+    for (int j = 0; j < W; j++) {
+        for (int r = 0; r < W; r++) {
+            vp[r] = vs + (size_t)r * n + j * m;
+            ep[r] = es + (size_t)r * ng + j * mg;
+        }
+        orc_dequant_accum_mx(W, vp, ep, m, red + j * m);
+        quant_mx_flat(red + j * m, m, v_final + j * m, e_final + j * mg);
+    }
+    for (int r = 0; r < W; r++)
+        for (int j = 0; j < W; j++)
+            dequant_mx_flat(v_final + j * m, e_final + j * mg, m, out[r] + j * m);
+    free(vs);
+    free(es);
+    free(vp);
+    free(ep);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -78,6 +78,21 @@ void orc_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                         int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
                         int64_t lds);
 
+/* ---- MXFP8 on the collective topologies (P2 Summary / Modes) ----------
+ * Flat layout: n E4M3 bytes and n/32 E8M0 bytes; group g = values [32g, 32g+32). */
+void orc_ring_hop_mx(const uint8_t* v_in, const uint8_t* e_in, const uint16_t* local,
+                     int64_t n, uint8_t* v_out, uint8_t* e_out);
+void orc_dequant_accum_mx(int nsrc, const uint8_t* const* v, const uint8_t* const* e8m0,
+                          int64_t n, uint16_t* y);
+void orc_a2a_reduce_mx(int nseg, int nsrc, const uint8_t* const* v_srcs,
+                       const uint8_t* const* e_srcs, int64_t seg_n, uint8_t* v_out,
+                       uint8_t* e_out, uint16_t* const* y_out, uint16_t* red);
+void orc_ring_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                           uint8_t* v_final, uint8_t* e_final, uint16_t* const* out);
+void orc_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                          uint16_t* red, uint8_t* v_final, uint8_t* e_final,
+                          uint16_t* const* out);
+
 /* ---- E4M3 128-block codec, the pre-existing format the INT8 codec
  *      replaces (P1 Summary / Why) ------------------------------------- */
 void orc_quant_e4m3_b128(const uint16_t* x, int64_t n, uint8_t* v, float* scale);

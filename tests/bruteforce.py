@@ -150,3 +150,36 @@ def e8m0_byte(amax: Fraction) -> int:
         if Fraction(2) ** e >= d:
             return e + 127
     return 254
+
+
+# ---- MXFP8 collectives ----------------------------------------------------------------
+
+def mx_group(values: list[Fraction], neg_zero: list[bool]):
+    """(byte, codes) of one 32-value group of binary32 values by the MXFP8 definition;
+    neg_zero[i] marks a value that is an IEEE negative zero."""
+    byte = e8m0_byte(max(abs(t) for t in values))
+    sc = Fraction(2) ** (byte - 127)
+    codes = [e4m3_nearest(rn32(t / sc), negative_zero=nz) for t, nz in zip(values, neg_zero)]
+    return byte, codes
+
+
+def mx_hop_group(codes_in, byte_in: int, local_bits):
+    """One group of the MX ring hop: binary32 sums of the dequantized payload and the bf16
+    local partial, requantized.  IEEE signed zeros: a sum is -0 only when both addends
+    are -0 (an exact zero sum of opposite values is +0 under round-to-nearest)."""
+    sc = Fraction(2) ** (byte_in - 127)
+    sums, negz = [], []
+    for c, h in zip(codes_in, local_bits):
+        dq = rn32(e4m3_value(c) * sc)
+        s = rn32(dq + bf16_bits_to_fraction(h))
+        sums.append(s)
+        negz.append(s == 0 and c == 0x80 and h == 0x8000)
+    return mx_group(sums, negz)
+
+
+def mx_accum_value(codes, bytes_) -> int:
+    """bf16 bits of the in-order binary32 sum of the sources' MX values (from +0)."""
+    acc = Fraction(0)
+    for c, b in zip(codes, bytes_):
+        acc = rn32(acc + rn32(e4m3_value(c) * Fraction(2) ** (b - 127)))
+    return fraction_to_bf16_bits(acc)

@@ -36,11 +36,22 @@ MUTANTS = [
      ["test_ring_hop_bruteforce_and_identities"]),
     ("zero block stores scale 1", "*scale = 0.0f;", "*scale = 1.0f;",
      ["test_i8_worked_examples"]),
-    ("MX dequant exponent sign flipped", "float val = ldexpf(orc_e4m3_decode(v[r * ldv + c]), e);",
-     "float val = ldexpf(orc_e4m3_decode(v[r * ldv + c]), -e);",
+    ("MX dequant exponent sign flipped", "return ldexpf(orc_e4m3_decode(code), (int)byte - 127);",
+     "return ldexpf(orc_e4m3_decode(code), 127 - (int)byte);",
      ["test_mx_dequant_matches_torch_decode"]),
     ("E4M3-b128 divides by 127", "float s = amax / E4M3_MAX;", "float s = amax / I8_QMAX;",
      ["test_e4m3_b128_worked_examples"]),
+    ("MX hop subtracts the local partial", "sums[i] = dq + lp;", "sums[i] = dq - lp;",
+     ["test_mx_ring_hop_bruteforce_and_identities"]),
+    ("MX accumulate in reverse source order", "for (int src = 0; src < nsrc; ++src) {",
+     "for (int src = nsrc - 1; src >= 0; --src) {", ["test_mx_accum_order_and_bruteforce"]),
+    ("MX ring chunk index off by one", "int chunk = mod(r - 1 - k, W);",
+     "int chunk = mod(r - k, W);", ["test_mx_ring_allreduce_exact_sums_and_canonical_payload"]),
+    ("E8M0 of an underflowed quotient left at byte 127", "if (d == 0.0f)", "if (d < 0.0f)",
+     ["test_e8m0_quotient_underflow_saturates_to_the_smallest_byte"]),
+    ("MX hop rounds the sums to bf16 first", "            sums[i] = dq + lp;",
+     "            sums[i] = orc_bf16_to_f32(orc_f32_to_bf16(dq + lp));",
+     ["test_mx_ring_hop_bruteforce_and_identities"]),
     ("A2A requantizes only the first shard", "for (int j = 0; j < W; j++) {\n        for (int s = 0; s < W; s++) {",
      "for (int j = 0; j < 1; j++) {\n        for (int s = 0; s < W; s++) {",
      ["test_a2a_requantizes_the_bf16_sum"]),

@@ -578,3 +578,149 @@ def test_a2a_reduce_is_accumulate_then_quantize_then_materialize():
     assert np.array_equal(dred, red) and np.array_equal(dq, q) and np.array_equal(ds, s)
     for j in range(W):
         assert np.array_equal(douts[j][j * m:(j + 1) * m], ys[j])
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP8 on the collective topologies (flat layout: group g = values [32g, 32g+32))
+# ---------------------------------------------------------------------------------------
+
+def test_e8m0_quotient_underflow_saturates_to_the_smallest_byte():
+    """For 0 < amax below 448 * 2^-150 the binary32 quotient amax/448 is 0; rounding toward
+    +infinity with finite saturation then gives the smallest E8M0 value, byte 0.  Swept
+    with the brute force over every binary32 octave at five significands each."""
+    L = oracle.lib()
+    for k in range(-149, 128):
+        for sig in (1.0, 1.0 + 2.0 ** -23, 1.75, 1.75 + 2.0 ** -23, 2.0 - 2.0 ** -23):
+            a = np.float32(sig * 2.0 ** k) if k > -127 else np.float32(2.0 ** k)
+            if not np.isfinite(a) or a == 0:
+                continue
+            assert L.orc_e8m0_scale(float(a)) == bf.e8m0_byte(Fraction(float(a))), (k, sig)
+    assert oracle.e8m0_scale(2.0 ** -149) == 0
+
+
+def _mx_groups(v, e, g):
+    return [int(c) for c in v[g * 32:(g + 1) * 32]], int(e[g])
+
+
+def test_mx_ring_hop_bruteforce_and_identities():
+    for trial in range(3):
+        x = workloads.rows(6, trial, 0, 1, 256)[0]
+        loc = workloads.rows(7, trial + 10, 0, 1, 256)[0]
+        v, e = oracle.quant_mx_flat(x)
+        v2, e2 = oracle.ring_hop_mx(v, e, loc)
+        for g in range(8):
+            codes, byte = _mx_groups(v, e, g)
+            wb, wc = bf.mx_hop_group(codes, byte, [int(h) for h in loc[g * 32:(g + 1) * 32]])
+            assert e2[g] == wb and list(v2[g * 32:(g + 1) * 32]) == wc, (trial, g)
+    # local == +0: the hop re-encodes the payload's own values.  The byte may drop an
+    # octave (a group whose largest code is below 256) but every value is unchanged.
+    x = workloads.rows(1, 0, 0, 4, 1024).reshape(-1)
+    v, e = oracle.quant_mx_flat(x)
+    v2, e2 = oracle.ring_hop_mx(v, e, np.zeros_like(x))
+    y, y2 = f32(oracle.dequant_mx_flat(v, e)), f32(oracle.dequant_mx_flat(v2, e2))
+    assert np.array_equal(y.astype(np.float64), y2.astype(np.float64))
+    assert np.all(e2 <= e) and np.any(e2 < e)
+    # local == -(payload values), exact in bf16 here: every sum is +0, so every group is
+    # the all-zero group (byte 127) with +0 codes.
+    dq = torch.from_numpy(v.copy()).view(torch.float8_e4m3fn).double().numpy() * \
+        2.0 ** (np.repeat(e, 32).astype(np.float64) - 127)
+    yb = oracle.dequant_mx_flat(v, e)
+    assert np.array_equal(f32(yb).astype(np.float64), dq)
+    v3, e3 = oracle.ring_hop_mx(v, e, yb ^ np.uint16(0x8000))
+    assert np.all(e3 == 127) and not v3.any()
+
+
+def test_mx_hop_signed_zeros():
+    """Only -0 + -0 is -0 under round-to-nearest; an E4M3 zero keeps that sign."""
+    v = np.zeros(128, np.uint8)
+    e = np.full(4, 127, np.uint8)
+    loc = np.zeros(128, np.uint16)
+    v[0], loc[0] = 0x80, 0x8000
+    v[1], loc[1] = 0x80, 0x0000
+    v[2], loc[2] = 0x00, 0x8000
+    v2, e2 = oracle.ring_hop_mx(v, e, loc)
+    assert list(v2[:3]) == [0x80, 0x00, 0x00] and e2[0] == 127
+
+
+def test_mx_accum_order_and_bruteforce():
+    """Sources are summed in array order: 448 - 448 + 2^-29 keeps the small term, while
+    448 + 2^-29 - 448 loses it (absorbed below half an ulp of 448)."""
+    n = 128
+    v = [np.zeros(n, np.uint8) for _ in range(3)]
+    e = [np.full(n // 32, 127, np.uint8) for _ in range(3)]
+    v[0][0], v[1][0] = 0x7E, 0xFE                  # +448, -448 at scale 2^0
+    v[2][0], e[2][0] = 0x38, 127 - 29               # E4M3 1.0 at scale 2^-29
+    assert oracle.dequant_accum_mx(v, e)[0] == 0x3100                     # 2^-29
+    assert oracle.dequant_accum_mx([v[0], v[2], v[1]], [e[0], e[2], e[1]])[0] == 0
+    rng = np.random.default_rng(5)
+    for W in (1, 2, 3, 5):
+        xs = [workloads.rows(6, r, 0, 1, 256)[0] for r in range(W)]
+        vs, es = zip(*[oracle.quant_mx_flat(x) for x in xs])
+        got = oracle.dequant_accum_mx(list(vs), list(es))
+        for i in rng.integers(0, 256, 48):
+            want = bf.mx_accum_value([int(vv[i]) for vv in vs], [int(ee[i // 32]) for ee in es])
+            assert got[i] == want, (W, i)
+
+
+def test_mx_a2a_reduce_is_accumulate_then_quantize_then_materialize():
+    W = 4
+    parts = [workloads.rows(3, r, 0, 8, 1024).reshape(-1) for r in range(W)]
+    vs, es = zip(*[oracle.quant_mx_flat(p) for p in parts])
+    v, e, ys, red = oracle.a2a_reduce_mx(list(vs), list(es), W)
+    m = parts[0].size // W
+    for j in range(W):
+        sm = oracle.dequant_accum_mx([vv[j * m:(j + 1) * m] for vv in vs],
+                                     [ee[j * m // 32:(j + 1) * m // 32] for ee in es])
+        assert np.array_equal(red[j * m:(j + 1) * m], sm)
+        wv, we = oracle.quant_mx_flat(sm)
+        assert np.array_equal(v[j * m:(j + 1) * m], wv)
+        assert np.array_equal(e[j * m // 32:(j + 1) * m // 32], we)
+        assert np.array_equal(ys[j], oracle.dequant_mx_flat(wv, we))
+    dred, dv, de, douts = oracle.a2a_allreduce_mx(parts)
+    assert np.array_equal(dred, red) and np.array_equal(dv, v) and np.array_equal(de, e)
+    for j in range(W):
+        assert np.array_equal(douts[j][j * m:(j + 1) * m], ys[j])
+
+
+def _small_int_partials(W: int, n: int, seed: int):
+    """Partials in {-2, ..., 2}: every partial sum s has |s| <= 2W <= 16 and at most 4
+    significant bits, so every MXFP8 quantization of the ring and the all-to-all is exact
+    (the group scale puts the amax in (224, 448], and E4M3 holds 4 significant bits)."""
+    rng = np.random.default_rng(seed)
+    return [rng.integers(-2, 3, n).astype(np.float64) for _ in range(W)]
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
+def test_mx_ring_allreduce_exact_sums_and_canonical_payload(W):
+    parts = _small_int_partials(W, W * 256, W)
+    exact = np.sum(parts, axis=0)
+    vf, ef, outs = oracle.ring_allreduce_mx([_to_bf16_exact(p) for p in parts])
+    assert np.array_equal(f32(outs[0]).astype(np.float64), exact)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.array_equal(outs[0], oracle.dequant_mx_flat(vf, ef))
+    wv, we = oracle.quant_mx_flat(_to_bf16_exact(exact))    # exact sums requantized
+    assert np.array_equal(vf, wv) and np.array_equal(ef, we)
+
+
+def test_mx_ring_schedule():
+    """W=2: chunk 0 is quantized by rank 1 and folded in by rank 0."""
+    parts = [workloads.rows(2, r, 0, 2, 512).reshape(-1) for r in range(2)]
+    h = parts[0].size // 2
+    v1, e1 = oracle.quant_mx_flat(parts[1][:h])
+    vh, eh = oracle.ring_hop_mx(v1, e1, parts[0][:h])
+    vf, ef, outs = oracle.ring_allreduce_mx(parts)
+    assert np.array_equal(vf[:h], vh) and np.array_equal(ef[:h // 32], eh)
+    assert np.array_equal(outs[1][:h], oracle.dequant_mx_flat(vh, eh))
+
+
+@pytest.mark.parametrize("W", [1, 2, 4, 8])
+def test_mx_a2a_allreduce_exact_sums(W):
+    parts = _small_int_partials(W, W * 256, 10 + W)
+    exact = np.sum(parts, axis=0)
+    red, vf, ef, outs = oracle.a2a_allreduce_mx([_to_bf16_exact(p) for p in parts])
+    assert np.array_equal(f32(red).astype(np.float64), exact)
+    assert np.array_equal(f32(outs[0]).astype(np.float64), exact)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.array_equal(outs[0], oracle.dequant_mx_flat(vf, ef))
