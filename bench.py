@@ -54,6 +54,8 @@ B_ACCUM = lambda w: 132 * w + 256
 B_A2A_REDUCE = lambda w: 132 * w + 132 + 256   # w sources in; payload + owner's bf16 out
 B_ALLGATHER_SKIP = lambda w: 132 + 256 * (w - 1)   # shared payload once; w-1 ranks write
 B_MX = 256 + 128 + 4       # bf16 in; E4M3 + 4 E8M0 bytes out (per 128 values)
+# the flat MXFP8 payload has the INT8 payload's 132 bytes per 128 values, so the MXFP8
+# collectives move the same bytes as their INT8 counterparts (B_HOP, B_A2A_REDUCE, ...)
 B_E4M3 = 256 + 132
 
 
@@ -95,16 +97,23 @@ class Step:
             b["mx_e"] = torch.empty((ROWS, W * COLS // 32), dtype=u8, device=dev)
             b["mx_y"] = torch.empty((ROWS, W * COLS), dtype=i16, device=dev)
             b["e4_v"], b["e4_s"], b["e4_y"] = e(N, u8), e(NB, f32), e(N, i16)
+            # the MXFP8 collectives (not part of the step; timed beside it)
+            b["mxw_v"], b["mxw_e"] = e(N, u8), e(N // 32, u8)
+            b["mxr_out"] = [e(N, i16) for _ in range(W)]
+            b["mx_send_v"] = [e(N, u8) for _ in range(W)]
+            b["mx_send_e"] = [e(N // 32, u8) for _ in range(W)]
+            b["mx_bc_v"], b["mx_bc_e"] = e(N, u8), e(N // 32, u8)
+            b["mxa_out"] = [e(N, i16) for _ in range(W)]
             self.sets.append(b)
         self.stream = torch.cuda.current_stream()
         sp = ctypes.c_void_p(self.stream.cuda_stream)
         A = lambda ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
         P = lambda t: t.data_ptr()
         MB = M // 128
-        self.calls, self.kernels = [], []
+        self.calls, self.kernels, self.next_kernels = [], [], []
         for b in self.sets:
             parts = b["parts"]
-            calls, kern = [], []
+            calls, kern, nxt = [], [], []
             xs = A([P(t) for t in parts])
             # i8_ring driver; and its kernels: rank r starts with chunk r-1 and at step k
             # folds chunk r-1-k into the payload it received
@@ -161,8 +170,33 @@ class Step:
                        (P(b["e4_v"]), P(b["e4_s"]), N, P(b["e4_y"]), sp))):
                 calls.append(c)
                 kern.append(c)
+            # MXFP8 ring and all-to-all (the mx_ring / mx_a2a modes) at the same shapes
+            v0 = A([P(b["mxw_v"]) + M * chunk(r, 0) for r in range(W)])
+            e0 = A([P(b["mxw_e"]) + (M // 32) * chunk(r, 0) for r in range(W)])
+            nxt.append(("quant_mx_flat x4", NB * B_MX, L.bq_quant_mx_batch, (W, x0, M, v0, e0, sp)))
+            for k in range(1, W):
+                lk = A([P(parts[r]) + 2 * M * chunk(r, k) for r in range(W)])
+                vk = A([P(b["mxw_v"]) + M * chunk(r, k) for r in range(W)])
+                ek = A([P(b["mxw_e"]) + (M // 32) * chunk(r, k) for r in range(W)])
+                nxt.append(("ring_hop_mx x4", NB * B_HOP, L.bq_ring_hop_mx_batch,
+                            (W, vk, ek, lk, M, vk, ek, sp)))
+            nxt.append(("allgather_dequant_mx x4", NB * B_DEQUANT_SHARED(W),
+                        L.bq_allgather_dequant_mx,
+                        (W, P(b["mxw_v"]), P(b["mxw_e"]), N, A([P(t) for t in b["mxr_out"]]), 0,
+                         sp)))
+            vsend, esend = A([P(t) for t in b["mx_send_v"]]), A([P(t) for t in b["mx_send_e"]])
+            mouts = A([P(t) for t in b["mxa_out"]])
+            nxt.append(("quant_mx_flat x4", W * NB * B_MX, L.bq_quant_mx_batch,
+                        (W, xs, N, vsend, esend, sp)))
+            mown = A([P(b["mxa_out"][j]) + 2 * M * j for j in range(W)])
+            nxt.append(("a2a_reduce_mx 4src x4 owners", NB * B_A2A_REDUCE(W), L.bq_a2a_reduce_mx,
+                        (W, W, vsend, esend, M, P(b["mx_bc_v"]), P(b["mx_bc_e"]), mown, None, sp)))
+            nxt.append(("allgather_dequant_mx x4 skip own", NB * B_ALLGATHER_SKIP(W),
+                        L.bq_allgather_dequant_mx,
+                        (W, P(b["mx_bc_v"]), P(b["mx_bc_e"]), N, mouts, 1, sp)))
             self.calls.append(calls)
             self.kernels.append(kern)
+            self.next_kernels.append(nxt)
         assert sum(c[1] for c in self.calls[0]) == sum(k[1] for k in self.kernels[0])
 
     @property
@@ -262,28 +296,38 @@ def main() -> int:
     # on the launch stream -- no event sits between two launches, so the average is
     # the kernel's own duration as a trace shows it.
     reps = max(10, args.steps // 4)
-    kinds = {}
-    for k, (name, nbytes, _, _) in enumerate(step.kernels[0]):
-        kinds.setdefault((name, nbytes), []).append(k)
-    per = {}
-    for (name, nbytes), idx in kinds.items():
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(step.stream)
-        for i in range(reps):
-            seq = step.kernels[i % len(step.kernels)]
-            _, _, fn, fargs = seq[idx[i % len(idx)]]
-            st = fn(*fargs)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st}")
-        e1.record(step.stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        gbs = nbytes / (us * 1e-6) / 1e9
-        per[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_step": len(idx),
-                                       "us_per_launch": us, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
-                                       "us_per_step": us * len(idx)}
+
+    def time_kinds(seqs):
+        kinds = {}
+        for k, (name, nbytes, _, _) in enumerate(seqs[0]):
+            kinds.setdefault((name, nbytes), []).append(k)
+        out = {}
+        for (name, nbytes), idx in kinds.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(step.stream)
+            for i in range(reps):
+                _, _, fn, fargs = seqs[i % len(seqs)][idx[i % len(idx)]]
+                st = fn(*fargs)
+                if st != 0:
+                    raise RuntimeError(f"{name}: status {st}")
+            e1.record(step.stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_step": len(idx),
+                                           "us_per_launch": us, "gbs": gbs,
+                                           "frac": gbs / HBM_PEAK_GBS, "us_per_step": us * len(idx)}
+        return out
+
+    per = time_kinds(step.kernels)
+    # the MXFP8 ring and all-to-all primitives (not part of the step), after a warmup pass
+    for seq in step.next_kernels:
+        for name, _, fn, fargs in seq:
+            if fn(*fargs) != 0:
+                raise RuntimeError(f"{name}: warmup failed")
+    per_next = time_kinds(step.next_kernels)
     dom_name = max(per, key=lambda k: per[k]["us_per_step"])
     dom = per[dom_name]
 
@@ -300,13 +344,21 @@ def main() -> int:
         return {"max_abs": float(d.max()), "rms": float(d.pow(2).mean().sqrt())}
 
     mx_in = torch.cat([p.view(ROWS, COLS) for p in b0["parts"]], dim=1)
+    bq.bq_ring_allreduce_mx(b0["parts"], b0["mxw_v"], b0["mxw_e"], b0["mxr_out"], n=N)
+    bq.bq_a2a_allreduce_mx(b0["parts"], b0["mx_send_v"], b0["mx_send_e"], None, b0["mx_bc_v"],
+                           b0["mx_bc_e"], b0["mxa_out"], n=N)
+    torch.cuda.synchronize()
     accuracy = {
         "i8_ring_vs_fp64_sum": err(f64(b0["ring_out"][0]), exact),
         "i8_a2a_vs_fp64_sum": err(f64(b0["a2a_out"][0]), exact),
+        "mx_ring_vs_fp64_sum": err(f64(b0["mxr_out"][0]), exact),
+        "mx_a2a_vs_fp64_sum": err(f64(b0["mxa_out"][0]), exact),
         "mxfp8_roundtrip": err(f64(b0["mx_y"].contiguous()), f64(mx_in.contiguous())),
         "e4m3_b128_roundtrip": err(f64(b0["e4_y"]), f64(b0["parts"][0])),
         "ranks_bit_identical": all(torch.equal(b0["ring_out"][0], o) for o in b0["ring_out"]) and
-        all(torch.equal(b0["a2a_out"][0], o) for o in b0["a2a_out"]),
+        all(torch.equal(b0["a2a_out"][0], o) for o in b0["a2a_out"]) and
+        all(torch.equal(b0["mxr_out"][0], o) for o in b0["mxr_out"]) and
+        all(torch.equal(b0["mxa_out"][0], o) for o in b0["mxa_out"]),
     }
     del exact, mx_in
 
@@ -345,6 +397,13 @@ def main() -> int:
                         "launches_per_step": v["launches_per_step"],
                         "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
                         "frac": round(v["frac"], 4)} for k, v in per.items()},
+        # the MXFP8 ring / all-to-all primitives at the same shapes, timed the same way;
+        # not part of the step and not in `value`
+        "next_kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
+                             "launches_per_pass": v["launches_per_step"],
+                             "us_per_launch": round(v["us_per_launch"], 2),
+                             "gbs": round(v["gbs"], 1), "frac": round(v["frac"], 4)}
+                         for k, v in per_next.items()},
     }
     line["accuracy"] = accuracy
     if not args.no_cpu_baseline:

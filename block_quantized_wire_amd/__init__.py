@@ -24,6 +24,9 @@ __all__ = [
     "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
     "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
     "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
+    "bq_quant_mx_batch", "bq_dequant_mx_batch", "bq_ring_hop_mx", "bq_ring_hop_mx_batch",
+    "bq_dequant_accum_mx", "bq_a2a_reduce_mx", "bq_allgather_dequant_mx",
+    "bq_ring_allreduce_mx", "bq_a2a_allreduce_mx",
     "bq_quant_e4m3_b128", "bq_dequant_e4m3_b128",
     "bq_wire_bytes_b128", "bq_status_str", "bq_version",
 ]
@@ -61,6 +64,15 @@ _SIGS = {
     "bq_dequant_mx": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
     "bq_quant_mx_slice": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
     "bq_mx_staging_bytes": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "bq_quant_mx_batch": [_I, _PP, _I64, _PP, _PP, _P],
+    "bq_dequant_mx_batch": [_I, _PP, _PP, _I64, _PP, _P],
+    "bq_ring_hop_mx": [_P, _P, _P, _I64, _P, _P, _P],
+    "bq_ring_hop_mx_batch": [_I, _PP, _PP, _PP, _I64, _PP, _PP, _P],
+    "bq_dequant_accum_mx": [_I, _PP, _PP, _I64, _P, _P],
+    "bq_a2a_reduce_mx": [_I, _I, _PP, _PP, _I64, _P, _P, _PP, _P, _P],
+    "bq_allgather_dequant_mx": [_I, _P, _P, _I64, _PP, _I, _P],
+    "bq_ring_allreduce_mx": [_I, _I64, _PP, _P, _P, _PP, _P],
+    "bq_a2a_allreduce_mx": [_I, _I64, _PP, _PP, _PP, _P, _P, _P, _PP, _P],
     "bq_quant_e4m3_b128": [_P, _I64, _P, _P, _P],
     "bq_dequant_e4m3_b128": [_P, _P, _I64, _P, _P],
 }
@@ -264,6 +276,75 @@ def bq_mx_staging_bytes(capacity_rows: int, total_cols: int) -> tuple[int, int]:
     _check("bq_mx_staging_bytes",
            _L().bq_mx_staging_bytes(capacity_rows, total_cols, ctypes.byref(vb), ctypes.byref(sb)))
     return vb.value, sb.value
+
+
+# ---- flat MXFP8 on the collective topologies (v: u8[n] E4M3, e8m0: u8[n/32]) -----------
+
+def bq_quant_mx_batch(xs, vs, es, n: int | None = None, stream=None) -> None:
+    n = _numel(xs[0]) if n is None else n
+    _check("bq_quant_mx_batch", _L().bq_quant_mx_batch(len(xs), _ptrs(xs), n, _ptrs(vs), _ptrs(es),
+                                                      _stream(stream)))
+
+
+def bq_dequant_mx_batch(vs, es, ys, n: int | None = None, stream=None) -> None:
+    n = _numel(ys[0]) if n is None else n
+    _check("bq_dequant_mx_batch", _L().bq_dequant_mx_batch(len(vs), _ptrs(vs), _ptrs(es), n,
+                                                          _ptrs(ys), _stream(stream)))
+
+
+def bq_ring_hop_mx(v_in, e_in, local, v_out, e_out, n: int | None = None, stream=None) -> None:
+    n = _numel(local) if n is None else n
+    _check("bq_ring_hop_mx", _L().bq_ring_hop_mx(_ptr(v_in), _ptr(e_in), _ptr(local), n,
+                                                _ptr(v_out), _ptr(e_out), _stream(stream)))
+
+
+def bq_ring_hop_mx_batch(v_in, e_in, local, v_out, e_out, n: int | None = None,
+                         stream=None) -> None:
+    n = _numel(local[0]) if n is None else n
+    _check("bq_ring_hop_mx_batch",
+           _L().bq_ring_hop_mx_batch(len(v_in), _ptrs(v_in), _ptrs(e_in), _ptrs(local), n,
+                                    _ptrs(v_out), _ptrs(e_out), _stream(stream)))
+
+
+def bq_dequant_accum_mx(v_srcs, e_srcs, y, n: int | None = None, stream=None) -> None:
+    n = _numel(y) if n is None else n
+    _check("bq_dequant_accum_mx",
+           _L().bq_dequant_accum_mx(len(v_srcs), _ptrs(v_srcs), _ptrs(e_srcs), n, _ptr(y),
+                                   _stream(stream)))
+
+
+def bq_a2a_reduce_mx(nseg: int, v_srcs, e_srcs, v_out, e_out, y_out=None, red=None,
+                     seg_n: int | None = None, stream=None) -> None:
+    seg_n = _numel(v_out) // nseg if seg_n is None else seg_n
+    ys = _ptrs(y_out) if y_out is not None else None
+    _check("bq_a2a_reduce_mx",
+           _L().bq_a2a_reduce_mx(nseg, len(v_srcs), _ptrs(v_srcs), _ptrs(e_srcs), seg_n,
+                                 _ptr(v_out), _ptr(e_out), ys, _ptr(red), _stream(stream)))
+
+
+def bq_allgather_dequant_mx(v, e8m0, outs, skip_own: bool = False, n: int | None = None,
+                            stream=None) -> None:
+    n = _numel(v) if n is None else n
+    _check("bq_allgather_dequant_mx",
+           _L().bq_allgather_dequant_mx(len(outs), _ptr(v), _ptr(e8m0), n, _ptrs(outs),
+                                        int(skip_own), _stream(stream)))
+
+
+def bq_ring_allreduce_mx(partials, v_wire, e_wire, outs, n: int | None = None,
+                         stream=None) -> None:
+    n = _numel(partials[0]) if n is None else n
+    _check("bq_ring_allreduce_mx",
+           _L().bq_ring_allreduce_mx(len(partials), n, _ptrs(partials), _ptr(v_wire), _ptr(e_wire),
+                                    _ptrs(outs), _stream(stream)))
+
+
+def bq_a2a_allreduce_mx(partials, v_send, e_send, red, v_bcast, e_bcast, outs,
+                        n: int | None = None, stream=None) -> None:
+    n = _numel(partials[0]) if n is None else n
+    _check("bq_a2a_allreduce_mx",
+           _L().bq_a2a_allreduce_mx(len(partials), n, _ptrs(partials), _ptrs(v_send), _ptrs(e_send),
+                                   _ptr(red), _ptr(v_bcast), _ptr(e_bcast), _ptrs(outs),
+                                   _stream(stream)))
 
 
 # ---- E4M3 128-block codec ------------------------------------------------------------------

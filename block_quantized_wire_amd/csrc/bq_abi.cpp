@@ -76,103 +76,65 @@ bool any_overlap(const Span* outs, int nout, const Span* ins, int nin) {
 // Largest number of spans any entry point checks at once (a2a: 4W+3 outputs, W inputs).
 constexpr int kMaxSpans = 4 * BQ_MAX_BATCH + 4;
 
-}  // namespace
+// ---- flat block formats on the wire ----------------------------------------------------
+//
+// Block INT8 and flat MXFP8 share one wire layout: n payload bytes (int8_t or uint8_t E4M3)
+// and 4 scale bytes per 128-value block (one float, or four E8M0 bytes), 16- and 4-byte
+// aligned.  The validation and the collective schedules below are therefore written once
+// over the payload type P and scale type S; the launchers are overloaded per codec.
 
-extern "C" {
-
-const char* bq_status_str(bq_status s) {
-    switch (s) {
-    case BQ_OK: return "ok";
-    case BQ_ERR_NULL: return "a required pointer is NULL";
-    case BQ_ERR_SIZE: return "a count or shape is negative or not a multiple of its block";
-    case BQ_ERR_ALIGN: return "a pointer or leading dimension breaks the alignment rules";
-    case BQ_ERR_BOUNDS: return "a leading dimension, offset or capacity does not fit";
-    case BQ_ERR_NSRC: return "a source, rank or segment count is out of range";
-    case BQ_ERR_ALIAS: return "an output overlaps an input or another output";
-    case BQ_ERR_LAUNCH: return "the HIP kernel launch failed";
-    }
-    return "unknown status";
-}
-
-const char* bq_version(void) { return "libblockq 0.1 (gfx950)"; }
-
-int64_t bq_wire_bytes_b128(int64_t n) {
-    if (n < 0 || n % kBlk != 0)
-        return -1;
-    return (n / kBlk) * 132;
-}
-
-bq_status bq_mx_staging_bytes(int64_t capacity_rows, int64_t total_cols, int64_t* value_bytes,
-                              int64_t* scale_bytes) {
-    if (!value_bytes || !scale_bytes)
-        return BQ_ERR_NULL;
-    if (capacity_rows < 0 || total_cols < 0 || total_cols % kBlk != 0)
-        return BQ_ERR_SIZE;
-    *value_bytes = capacity_rows * total_cols;
-    *scale_bytes = capacity_rows * (total_cols / BQ_MX_GROUP);
-    return BQ_OK;
-}
-
-// ---- block INT8 ----------------------------------------------------------------------
-
-bq_status bq_quant_i8_batch(int count, const uint16_t* const* x, int64_t n, int8_t* const* q,
-                            float* const* scale, void* stream) {
+template <typename P, typename S>
+bq_status quant_batch(int count, const uint16_t* const* x, int64_t n, P* const* q, S* const* s,
+                      void* stream) {
     if (count < 1 || count > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
     BQ_TRY(check_n(n));
     if (n == 0)
         return BQ_OK;
-    if (!x || !q || !scale)
+    if (!x || !q || !s)
         return BQ_ERR_NULL;
     Span outs[2 * BQ_MAX_BATCH], ins[BQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
         BQ_TRY(check_bf16(x[i]));
         BQ_TRY(check_payload(q[i]));
-        BQ_TRY(check_scales(scale[i]));
+        BQ_TRY(check_scales(s[i]));
         ins[i] = span(x[i], 2 * n);
         outs[2 * i] = span(q[i], n);
-        outs[2 * i + 1] = span(scale[i], 4 * (n / kBlk));
+        outs[2 * i + 1] = span(s[i], 4 * (n / kBlk));
     }
     if (any_overlap(outs, 2 * count, ins, count))
         return BQ_ERR_ALIAS;
-    return launched(bq::launch_quant_i8(count, x, q, scale, n, as_stream(stream)));
+    return launched(bq::launch_quant(count, x, q, s, n, as_stream(stream)));
 }
 
-bq_status bq_quant_i8(const uint16_t* x, int64_t n, int8_t* q, float* scale, void* stream) {
-    return bq_quant_i8_batch(1, &x, n, &q, &scale, stream);
-}
-
-bq_status bq_dequant_i8_batch(int count, const int8_t* const* q, const float* const* scale,
-                              int64_t n, uint16_t* const* y, void* stream) {
+template <typename P, typename S>
+bq_status dequant_batch(int count, const P* const* q, const S* const* s, int64_t n,
+                        uint16_t* const* y, void* stream) {
     if (count < 1 || count > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
     BQ_TRY(check_n(n));
     if (n == 0)
         return BQ_OK;
-    if (!q || !scale || !y)
+    if (!q || !s || !y)
         return BQ_ERR_NULL;
     Span outs[BQ_MAX_BATCH], ins[2 * BQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
         BQ_TRY(check_payload(q[i]));
-        BQ_TRY(check_scales(scale[i]));
+        BQ_TRY(check_scales(s[i]));
         BQ_TRY(check_bf16(y[i]));
         ins[2 * i] = span(q[i], n);
-        ins[2 * i + 1] = span(scale[i], 4 * (n / kBlk));
+        ins[2 * i + 1] = span(s[i], 4 * (n / kBlk));
         outs[i] = span(y[i], 2 * n);
     }
     if (any_overlap(outs, count, ins, 2 * count))
         return BQ_ERR_ALIAS;
-    return launched(bq::launch_dequant_i8(count, q, scale, y, n, as_stream(stream)));
+    return launched(bq::launch_dequant(count, q, s, y, n, as_stream(stream)));
 }
 
-bq_status bq_dequant_i8(const int8_t* q, const float* scale, int64_t n, uint16_t* y,
-                        void* stream) {
-    return bq_dequant_i8_batch(1, &q, &scale, n, &y, stream);
-}
-
-bq_status bq_ring_hop_i8_batch(int count, const int8_t* const* q_in, const float* const* s_in,
-                               const uint16_t* const* local, int64_t n, int8_t* const* q_out,
-                               float* const* s_out, void* stream) {
+template <typename P, typename S>
+bq_status ring_hop_batch(int count, const P* const* q_in, const S* const* s_in,
+                         const uint16_t* const* local, int64_t n, P* const* q_out,
+                         S* const* s_out, void* stream) {
     if (count < 1 || count > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
     BQ_TRY(check_n(n));
@@ -218,17 +180,12 @@ bq_status bq_ring_hop_i8_batch(int count, const int8_t* const* q_in, const float
         }
     }
     return launched(
-        bq::launch_ring_hop_i8(count, q_in, s_in, local, q_out, s_out, n, as_stream(stream)));
+        bq::launch_ring_hop(count, q_in, s_in, local, q_out, s_out, n, as_stream(stream)));
 }
 
-bq_status bq_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* local,
-                         int64_t n, int8_t* q_out, float* s_out, void* stream) {
-    return bq_ring_hop_i8_batch(1, &q_in, &s_in, &local, n, &q_out, &s_out, stream);
-}
-
-bq_status bq_dequant_accum_i8_batch(int nseg, int nsrc, const int8_t* const* q_srcs,
-                                    const float* const* s_srcs, int64_t seg_n, uint16_t* y,
-                                    void* stream) {
+template <typename P, typename S>
+bq_status accum_batch(int nseg, int nsrc, const P* const* q_srcs, const S* const* s_srcs,
+                      int64_t seg_n, uint16_t* y, void* stream) {
     if (nsrc < 1 || nsrc > BQ_MAX_SRC || nseg < 1 || nseg > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
     BQ_TRY(check_n(seg_n));
@@ -245,17 +202,13 @@ bq_status bq_dequant_accum_i8_batch(int nseg, int nsrc, const int8_t* const* q_s
         if (overlaps(ys, span(q_srcs[i], n)) || overlaps(ys, span(s_srcs[i], 4 * (n / kBlk))))
             return BQ_ERR_ALIAS;
     }
-    return launched(bq::launch_accum_i8(nsrc, q_srcs, s_srcs, y, nseg, seg_n, as_stream(stream)));
+    return launched(bq::launch_accum(nsrc, q_srcs, s_srcs, y, nseg, seg_n, as_stream(stream)));
 }
 
-bq_status bq_dequant_accum_i8(int nsrc, const int8_t* const* q_srcs, const float* const* s_srcs,
-                              int64_t n, uint16_t* y, void* stream) {
-    return bq_dequant_accum_i8_batch(1, nsrc, q_srcs, s_srcs, n, y, stream);
-}
-
-bq_status bq_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
-                           const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
-                           float* s_out, uint16_t* const* y_out, uint16_t* red, void* stream) {
+template <typename P, typename S>
+bq_status a2a_reduce(int nseg, int nsrc, const P* const* q_srcs, const S* const* s_srcs,
+                     int64_t seg_n, P* q_out, S* s_out, uint16_t* const* y_out, uint16_t* red,
+                     void* stream) {
     if (nsrc < 1 || nsrc > BQ_MAX_SRC || nseg < 1 || nseg > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
     BQ_TRY(check_n(seg_n));
@@ -289,14 +242,13 @@ bq_status bq_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
     }
     if (any_overlap(outs, no, ins, 2 * nsrc))
         return BQ_ERR_ALIAS;
-    return launched(bq::launch_a2a_reduce_i8(nsrc, q_srcs, s_srcs, nseg, seg_n, q_out, s_out,
-                                             y_out, red, as_stream(stream)));
+    return launched(bq::launch_a2a_reduce(nsrc, q_srcs, s_srcs, nseg, seg_n, q_out, s_out, y_out,
+                                          red, as_stream(stream)));
 }
 
-// ---- collectives on one GPU ------------------------------------------------------------
-
-bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, int64_t n,
-                                  uint16_t* const* out, int skip_own, void* stream) {
+template <typename P, typename S>
+bq_status allgather_dequant(int world, const P* q, const S* s, int64_t n, uint16_t* const* out,
+                            int skip_own, void* stream) {
     const int W = world;
     if (W < 1 || W > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
@@ -316,19 +268,22 @@ bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, in
     }
     if (any_overlap(outs, W, ins, 2))
         return BQ_ERR_ALIAS;
-    const int8_t* qi[BQ_MAX_BATCH];
-    const float* si[BQ_MAX_BATCH];
+    const P* qi[BQ_MAX_BATCH];
+    const S* si[BQ_MAX_BATCH];
     for (int r = 0; r < W; ++r) {
         qi[r] = q;
         si[r] = s;
     }
-    return launched(bq::launch_dequant_i8(W, qi, si, out, n, as_stream(stream),
-                                          skip_own ? n / W : 0));
+    return launched(bq::launch_dequant(W, qi, si, out, n, as_stream(stream), skip_own ? n / W : 0));
 }
 
-bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
-                               int8_t* q_wire, float* s_wire, uint16_t* const* out,
-                               void* stream) {
+// The ring all-reduce (P1 Summary; P2 Modes for the MXFP8 codec).  Chunk c of n/W values
+// is quantized at step 0 by rank c+1, folded in by one hop per later step, and every rank
+// materializes every chunk from its final payload.  Scale arrays hold 4 bytes per block,
+// so a chunk's scales start at byte 4 * (c*n/W)/128 for either codec.
+template <typename P, typename S>
+bq_status ring_allreduce(int world, int64_t n, const uint16_t* const* partials, P* q_wire,
+                         S* s_wire, uint16_t* const* out, void* stream) {
     const int W = world;
     if (W < 1 || W > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
@@ -354,29 +309,30 @@ bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* part
         return BQ_ERR_ALIAS;
 
     const hipStream_t st = as_stream(stream);
-    const int64_t m = n / W, mb = m / kBlk;
+    const int64_t m = n / W;
+    const int64_t ms = (m / kBlk) * 4 / (int64_t)sizeof(S);   // scale elements per chunk
     const uint16_t* x[BQ_MAX_BATCH];
-    const int8_t* qi[BQ_MAX_BATCH];
-    const float* si[BQ_MAX_BATCH];
-    int8_t* qo[BQ_MAX_BATCH];
-    float* so[BQ_MAX_BATCH];
+    const P* qi[BQ_MAX_BATCH];
+    const S* si[BQ_MAX_BATCH];
+    P* qo[BQ_MAX_BATCH];
+    S* so[BQ_MAX_BATCH];
     // step 0: rank r quantizes its partial of chunk (r-1) mod W
     for (int r = 0; r < W; ++r) {
         const int c = (r - 1 + W) % W;
         x[r] = partials[r] + c * m;
         qo[r] = q_wire + c * m;
-        so[r] = s_wire + c * mb;
+        so[r] = s_wire + c * ms;
     }
-    bq_status stt = launched(bq::launch_quant_i8(W, x, qo, so, m, st));
+    bq_status stt = launched(bq::launch_quant(W, x, qo, so, m, st));
     // steps 1..W-1: rank r folds its partial of chunk (r-1-k) mod W into that payload
     for (int k = 1; k < W && stt == BQ_OK; ++k) {
         for (int r = 0; r < W; ++r) {
             const int c = ((r - 1 - k) % W + W) % W;
             x[r] = partials[r] + c * m;
             qi[r] = qo[r] = q_wire + c * m;
-            si[r] = so[r] = s_wire + c * mb;
+            si[r] = so[r] = s_wire + c * ms;
         }
-        stt = launched(bq::launch_ring_hop_i8(W, qi, si, x, qo, so, m, st));
+        stt = launched(bq::launch_ring_hop(W, qi, si, x, qo, so, m, st));
     }
     // all-gather: every rank materializes every chunk from the same final payloads
     if (stt == BQ_OK) {
@@ -384,15 +340,16 @@ bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* part
             qi[r] = q_wire;
             si[r] = s_wire;
         }
-        stt = launched(bq::launch_dequant_i8(W, qi, si, out, n, st));
+        stt = launched(bq::launch_dequant(W, qi, si, out, n, st));
     }
     return stt;
 }
 
-bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
-                              int8_t* const* q_send, float* const* s_send, uint16_t* red,
-                              int8_t* q_bcast, float* s_bcast, uint16_t* const* out,
-                              void* stream) {
+// The quantize-once all-to-all (P1 Summary, Implementation; P2 Modes for MXFP8).
+template <typename P, typename S>
+bq_status a2a_allreduce(int world, int64_t n, const uint16_t* const* partials, P* const* q_send,
+                        S* const* s_send, uint16_t* red, P* q_bcast, S* s_bcast,
+                        uint16_t* const* out, void* stream) {
     const int W = world;
     if (W < 1 || W > BQ_MAX_BATCH)
         return BQ_ERR_NSRC;
@@ -430,26 +387,184 @@ bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* parti
     const hipStream_t st = as_stream(stream);
     const int64_t m = n / W;
     // quantize every partial once
-    bq_status stt = launched(bq::launch_quant_i8(W, partials, q_send, s_send, n, st));
+    bq_status stt = launched(bq::launch_quant(W, partials, q_send, s_send, n, st));
     // owner j accumulates shard j of every payload in rank order, requantizes its bf16
     // sum once into the broadcast payload and materializes its own shard from it
     uint16_t* own[BQ_MAX_BATCH];
     for (int j = 0; j < W; ++j)
         own[j] = out[j] + j * m;
     if (stt == BQ_OK)
-        stt = launched(bq::launch_a2a_reduce_i8(W, q_send, s_send, W, m, q_bcast, s_bcast, own,
-                                                red, st));
+        stt = launched(bq::launch_a2a_reduce(W, q_send, s_send, W, m, q_bcast, s_bcast, own, red,
+                                             st));
     // every rank materializes the other owners' shards from the broadcast payload
     if (stt == BQ_OK && W > 1) {
-        const int8_t* qi[BQ_MAX_BATCH];
-        const float* si[BQ_MAX_BATCH];
+        const P* qi[BQ_MAX_BATCH];
+        const S* si[BQ_MAX_BATCH];
         for (int r = 0; r < W; ++r) {
             qi[r] = q_bcast;
             si[r] = s_bcast;
         }
-        stt = launched(bq::launch_dequant_i8(W, qi, si, out, n, st, m));
+        stt = launched(bq::launch_dequant(W, qi, si, out, n, st, m));
     }
     return stt;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bq_status_str(bq_status s) {
+    switch (s) {
+    case BQ_OK: return "ok";
+    case BQ_ERR_NULL: return "a required pointer is NULL";
+    case BQ_ERR_SIZE: return "a count or shape is negative or not a multiple of its block";
+    case BQ_ERR_ALIGN: return "a pointer or leading dimension breaks the alignment rules";
+    case BQ_ERR_BOUNDS: return "a leading dimension, offset or capacity does not fit";
+    case BQ_ERR_NSRC: return "a source, rank or segment count is out of range";
+    case BQ_ERR_ALIAS: return "an output overlaps an input or another output";
+    case BQ_ERR_LAUNCH: return "the HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* bq_version(void) { return "libblockq 0.1 (gfx950)"; }
+
+int64_t bq_wire_bytes_b128(int64_t n) {
+    if (n < 0 || n % kBlk != 0)
+        return -1;
+    return (n / kBlk) * 132;
+}
+
+bq_status bq_mx_staging_bytes(int64_t capacity_rows, int64_t total_cols, int64_t* value_bytes,
+                              int64_t* scale_bytes) {
+    if (!value_bytes || !scale_bytes)
+        return BQ_ERR_NULL;
+    if (capacity_rows < 0 || total_cols < 0 || total_cols % kBlk != 0)
+        return BQ_ERR_SIZE;
+    *value_bytes = capacity_rows * total_cols;
+    *scale_bytes = capacity_rows * (total_cols / BQ_MX_GROUP);
+    return BQ_OK;
+}
+
+// ---- block INT8 ----------------------------------------------------------------------
+
+bq_status bq_quant_i8_batch(int count, const uint16_t* const* x, int64_t n, int8_t* const* q,
+                            float* const* scale, void* stream) {
+    return quant_batch(count, x, n, q, scale, stream);
+}
+
+bq_status bq_quant_i8(const uint16_t* x, int64_t n, int8_t* q, float* scale, void* stream) {
+    return quant_batch(1, &x, n, &q, &scale, stream);
+}
+
+bq_status bq_dequant_i8_batch(int count, const int8_t* const* q, const float* const* scale,
+                              int64_t n, uint16_t* const* y, void* stream) {
+    return dequant_batch(count, q, scale, n, y, stream);
+}
+
+bq_status bq_dequant_i8(const int8_t* q, const float* scale, int64_t n, uint16_t* y,
+                        void* stream) {
+    return dequant_batch(1, &q, &scale, n, &y, stream);
+}
+
+bq_status bq_ring_hop_i8_batch(int count, const int8_t* const* q_in, const float* const* s_in,
+                               const uint16_t* const* local, int64_t n, int8_t* const* q_out,
+                               float* const* s_out, void* stream) {
+    return ring_hop_batch(count, q_in, s_in, local, n, q_out, s_out, stream);
+}
+
+bq_status bq_ring_hop_i8(const int8_t* q_in, const float* s_in, const uint16_t* local,
+                         int64_t n, int8_t* q_out, float* s_out, void* stream) {
+    return ring_hop_batch(1, &q_in, &s_in, &local, n, &q_out, &s_out, stream);
+}
+
+bq_status bq_dequant_accum_i8_batch(int nseg, int nsrc, const int8_t* const* q_srcs,
+                                    const float* const* s_srcs, int64_t seg_n, uint16_t* y,
+                                    void* stream) {
+    return accum_batch(nseg, nsrc, q_srcs, s_srcs, seg_n, y, stream);
+}
+
+bq_status bq_dequant_accum_i8(int nsrc, const int8_t* const* q_srcs, const float* const* s_srcs,
+                              int64_t n, uint16_t* y, void* stream) {
+    return accum_batch(1, nsrc, q_srcs, s_srcs, n, y, stream);
+}
+
+bq_status bq_a2a_reduce_i8(int nseg, int nsrc, const int8_t* const* q_srcs,
+                           const float* const* s_srcs, int64_t seg_n, int8_t* q_out,
+                           float* s_out, uint16_t* const* y_out, uint16_t* red, void* stream) {
+    return a2a_reduce(nseg, nsrc, q_srcs, s_srcs, seg_n, q_out, s_out, y_out, red, stream);
+}
+
+bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, int64_t n,
+                                  uint16_t* const* out, int skip_own, void* stream) {
+    return allgather_dequant(world, q, s, n, out, skip_own, stream);
+}
+
+bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                               int8_t* q_wire, float* s_wire, uint16_t* const* out,
+                               void* stream) {
+    return ring_allreduce(world, n, partials, q_wire, s_wire, out, stream);
+}
+
+bq_status bq_a2a_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
+                              int8_t* const* q_send, float* const* s_send, uint16_t* red,
+                              int8_t* q_bcast, float* s_bcast, uint16_t* const* out,
+                              void* stream) {
+    return a2a_allreduce(world, n, partials, q_send, s_send, red, q_bcast, s_bcast, out, stream);
+}
+
+// ---- flat MXFP8 on the collective topologies ---------------------------------------------
+
+bq_status bq_quant_mx_batch(int count, const uint16_t* const* x, int64_t n, uint8_t* const* v,
+                            uint8_t* const* e8m0, void* stream) {
+    return quant_batch(count, x, n, v, e8m0, stream);
+}
+
+bq_status bq_dequant_mx_batch(int count, const uint8_t* const* v, const uint8_t* const* e8m0,
+                              int64_t n, uint16_t* const* y, void* stream) {
+    return dequant_batch(count, v, e8m0, n, y, stream);
+}
+
+bq_status bq_ring_hop_mx_batch(int count, const uint8_t* const* v_in,
+                               const uint8_t* const* e_in, const uint16_t* const* local,
+                               int64_t n, uint8_t* const* v_out, uint8_t* const* e_out,
+                               void* stream) {
+    return ring_hop_batch(count, v_in, e_in, local, n, v_out, e_out, stream);
+}
+
+bq_status bq_ring_hop_mx(const uint8_t* v_in, const uint8_t* e_in, const uint16_t* local,
+                         int64_t n, uint8_t* v_out, uint8_t* e_out, void* stream) {
+    return ring_hop_batch(1, &v_in, &e_in, &local, n, &v_out, &e_out, stream);
+}
+
+bq_status bq_dequant_accum_mx(int nsrc, const uint8_t* const* v_srcs,
+                              const uint8_t* const* e_srcs, int64_t n, uint16_t* y,
+                              void* stream) {
+    return accum_batch(1, nsrc, v_srcs, e_srcs, n, y, stream);
+}
+
+bq_status bq_a2a_reduce_mx(int nseg, int nsrc, const uint8_t* const* v_srcs,
+                           const uint8_t* const* e_srcs, int64_t seg_n, uint8_t* v_out,
+                           uint8_t* e_out, uint16_t* const* y_out, uint16_t* red, void* stream) {
+    return a2a_reduce(nseg, nsrc, v_srcs, e_srcs, seg_n, v_out, e_out, y_out, red, stream);
+}
+
+bq_status bq_allgather_dequant_mx(int world, const uint8_t* v, const uint8_t* e8m0, int64_t n,
+                                  uint16_t* const* out, int skip_own, void* stream) {
+    return allgather_dequant(world, v, e8m0, n, out, skip_own, stream);
+}
+
+bq_status bq_ring_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                               uint8_t* v_wire, uint8_t* e_wire, uint16_t* const* out,
+                               void* stream) {
+    return ring_allreduce(world, n, partials, v_wire, e_wire, out, stream);
+}
+
+bq_status bq_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                              uint8_t* const* v_send, uint8_t* const* e_send, uint16_t* red,
+                              uint8_t* v_bcast, uint8_t* e_bcast, uint16_t* const* out,
+                              void* stream) {
+    return a2a_allreduce(world, n, partials, v_send, e_send, red, v_bcast, e_bcast, out, stream);
 }
 
 // ---- MXFP8 --------------------------------------------------------------------------------

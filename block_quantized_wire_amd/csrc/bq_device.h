@@ -261,10 +261,78 @@ __device__ __forceinline__ uint32_t e8m0_from_bf16_amax(uint32_t h) {
     return (uint32_t)(e < 0 ? 0 : e);
 }
 
+// MXFP8 shared-scale byte from a binary32 amax >= 0 (the binary32 sums of a ring hop):
+// 127 for amax == 0; else 127 + (smallest e with 2^e >= t), t = fl32(amax/448), clamped to
+// [-127, 127].  t is taken from the fp64 product amax * fl64(1/448).  For a normal t that
+// product rounds to fl32(amax/448) itself (the period-3 argument of the header holds for
+// every binary32 numerator; an exact quotient stays exact), and the byte is the biased
+// exponent plus one unless the significand bits are zero.  For t below 2^-126 the byte
+// is 1 when t > 2^-127 and 0 otherwise; there the product can differ from fl32(amax/448)
+// only at a tie between two subnormals, and no binary32 amax puts a tie next to 2^-127
+// (it would need a 26-bit odd significand), so the byte is exact for every amax.
+__device__ __forceinline__ uint32_t e8m0_from_f32_amax(float amax) {
+    if (amax == 0.0f)
+        return 127u;
+    const uint32_t b = __float_as_uint((float)((double)amax * (1.0 / 448.0)));
+    if (b >= 0x00800000u)
+        return (b + 0x007FFFFFu) >> 23;
+    return b > 0x00400000u ? 1u : 0u;
+}
+
+// 2^(byte - 127) as binary32: a normal number for byte >= 1, the subnormal 2^-127 for
+// byte 0 (any E4M3 value times it is exact: the codes are multiples of 2^-9).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+    return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+}
+
 // 2^(127 - byte) as binary32 for byte in [0, 254] (always a normal number here since
 // the quantizer never produces a byte above 247).
 __device__ __forceinline__ float e8m0_inv_scale(uint32_t byte) {
     return __uint_as_float((254u - byte) << 23);
+}
+
+// ---- lane walk -----------------------------------------------------------------------
+
+// Lane bookkeeping of the flat kernels (one 128-value block per DPP row): the lane's
+// block within a tile and its first value in that block.  Waves walk the tiles
+// grid-stride, U adjacent tiles per step, so a launch needs no more workgroups than
+// the chip holds at once.
+// The wave index is read from the first lane, so the tile a wave works on is a uniform
+// (scalar) value: each access is a scalar base of the step plus a small 32-bit lane
+// offset, which keeps addresses out of the vector registers.
+struct Lanes {
+    uint32_t sub, off;
+    bool leader;     // first lane of the row: stores the block's scale
+    int64_t first;   // first tile of this wave
+    int64_t step;    // tiles between successive steps of this wave
+    __device__ explicit Lanes(int U) {
+        const uint32_t lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        sub = lane >> 4;
+        off = (lane & 15) * kLaneVals;
+        leader = (lane & 15) == 0;
+        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        step = (int64_t)gridDim.x * kWavesPerGroup * U;
+    }
+    // MXFP8 group (0..3) of the lane's 8 values within its block: one quad per group
+    __device__ __forceinline__ uint32_t grp() const { return off >> 5; }
+    // block of tile u of a step, counted from the step's first block
+    __device__ __forceinline__ uint32_t blk(int u) const { return (uint32_t)u * kTileBlocks + sub; }
+    // first value of this lane in tile u of a step, counted from the step's first value
+    __device__ __forceinline__ uint32_t val(int u) const { return blk(u) * kBlock + off; }
+};
+
+__device__ __forceinline__ int64_t tiles_of(int64_t nb) { return (nb + kTileBlocks - 1) / kTileBlocks; }
+
+// Launch shape of the flat kernels: 256-thread workgroups of 4 waves, U tiles of 4
+// blocks per wave step; at most kMaxGroups workgroups in all (the `count` segments of a
+// batch, grid.y, share them).
+template <int U>
+dim3 grid_for(int64_t nb, int count) {
+    const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
+    const int64_t want = (nb + per_group - 1) / per_group;
+    const int64_t cap = kMaxGroups / count > 0 ? kMaxGroups / count : 1;
+    return dim3((unsigned)(want < cap ? want : cap), (unsigned)count, 1);
 }
 
 }  // namespace bq

@@ -58,34 +58,6 @@ struct AccumArgs {
     int64_t seg_n;            // values per segment
 };
 
-// Lane bookkeeping common to all INT8 kernels: the lane's block within a tile (its DPP
-// row) and its first value in that block.  Waves walk the tiles grid-stride, U adjacent
-// tiles per step, so a launch needs no more workgroups than the chip holds at once.
-// The wave index is read from the first lane, so the tile a wave works on is a uniform
-// (scalar) value: each access is a scalar base of the step plus a small 32-bit lane
-// offset, which keeps addresses out of the vector registers.
-struct Lanes {
-    uint32_t sub, off;
-    bool leader;     // first lane of the row: stores the block's scale
-    int64_t first;   // first tile of this wave
-    int64_t step;    // tiles between successive steps of this wave
-    __device__ explicit Lanes(int U) {
-        const uint32_t lane = threadIdx.x & 63;
-        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-        sub = lane >> 4;
-        off = (lane & 15) * kLaneVals;
-        leader = (lane & 15) == 0;
-        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
-        step = (int64_t)gridDim.x * kWavesPerGroup * U;
-    }
-    // block of tile u of a step, counted from the step's first block
-    __device__ __forceinline__ uint32_t blk(int u) const { return (uint32_t)u * kTileBlocks + sub; }
-    // first value of this lane in tile u of a step, counted from the step's first value
-    __device__ __forceinline__ uint32_t val(int u) const { return blk(u) * kBlock + off; }
-};
-
-__device__ __forceinline__ int64_t tiles_of(int64_t nb) { return (nb + kTileBlocks - 1) / kTileBlocks; }
-
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
@@ -283,16 +255,6 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     }
 }
 
-// Launch shape: 256-thread workgroups of 4 waves, U tiles of 4 blocks per wave step;
-// at most kMaxGroups workgroups in all (the segments of a batch share them).
-template <int U>
-dim3 grid_for(int64_t nb, int count) {
-    const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
-    const int64_t want = (nb + per_group - 1) / per_group;
-    const int64_t cap = kMaxGroups / count > 0 ? kMaxGroups / count : 1;
-    return dim3((unsigned)(want < cap ? want : cap), (unsigned)count, 1);
-}
-
 constexpr int kUQuant = 2;
 constexpr int kUDequant = 2;
 constexpr int kUHop = 2;
@@ -300,7 +262,7 @@ constexpr int kUAccum = 2;
 
 }  // namespace
 
-hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
+hipError_t launch_quant(int count, const uint16_t* const* x, int8_t* const* q,
                            float* const* s, int64_t n, hipStream_t stream) {
     QuantArgs a{};
     for (int i = 0; i < count; ++i) {
@@ -312,7 +274,7 @@ hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q
     return launch1(k_quant_i8<kUQuant>, grid_for<kUQuant>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
-hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
+hipError_t launch_dequant(int count, const int8_t* const* q, const float* const* s,
                              uint16_t* const* y, int64_t n, hipStream_t stream,
                              int64_t skip_shard_n) {
     DequantArgs a{};
@@ -329,7 +291,7 @@ hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* con
     return launch1(k_dequant_i8<kUDequant, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
-hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
+hipError_t launch_ring_hop(int count, const int8_t* const* q_in, const float* const* s_in,
                               const uint16_t* const* local, int8_t* const* q_out,
                               float* const* s_out, int64_t n, hipStream_t stream) {
     HopArgs a{};
@@ -344,7 +306,7 @@ hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float*
     return launch1(k_ring_hop_i8<kUHop>, grid_for<kUHop>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
-hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
+hipError_t launch_accum(int nsrc, const int8_t* const* q, const float* const* s,
                            uint16_t* y, int nseg, int64_t seg_n, hipStream_t stream) {
     AccumArgs a{};
     for (int i = 0; i < nsrc; ++i) {
@@ -359,7 +321,7 @@ hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const*
                    dim3(kGroupThreads), stream, a);
 }
 
-hipError_t launch_a2a_reduce_i8(int nsrc, const int8_t* const* q, const float* const* s,
+hipError_t launch_a2a_reduce(int nsrc, const int8_t* const* q, const float* const* s,
                                 int nseg, int64_t seg_n, int8_t* q_out, float* s_out,
                                 uint16_t* const* y, uint16_t* red, hipStream_t stream) {
     AccumArgs a{};

@@ -19,27 +19,43 @@ hipError_t launch1(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t strea
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
 }
 
-// Block INT8.  Segment i of a batch is (x[i] -> q[i], s[i]), n values each.
-hipError_t launch_quant_i8(int count, const uint16_t* const* x, int8_t* const* q,
-                           float* const* s, int64_t n, hipStream_t stream);
+// Flat block formats on the wire, one overload per codec (selected by the payload and
+// scale pointer types): block INT8 (int8_t payload, one float scale per 128 values)
+// and flat MXFP8 (uint8_t E4M3 payload, one uint8_t E8M0 byte per 32 values).  Both
+// are 132 bytes per 128 values.  Segment i of a batch is (x[i] -> q[i], s[i]), n values.
+hipError_t launch_quant(int count, const uint16_t* const* x, int8_t* const* q, float* const* s,
+                        int64_t n, hipStream_t stream);
+hipError_t launch_quant(int count, const uint16_t* const* x, uint8_t* const* v,
+                        uint8_t* const* e, int64_t n, hipStream_t stream);
 // skip_shard_n > 0: segment i leaves values [i*skip_shard_n, (i+1)*skip_shard_n) of
 // its output untouched (the shard an all-to-all owner has already materialized).
-hipError_t launch_dequant_i8(int count, const int8_t* const* q, const float* const* s,
-                             uint16_t* const* y, int64_t n, hipStream_t stream,
-                             int64_t skip_shard_n = 0);
-hipError_t launch_ring_hop_i8(int count, const int8_t* const* q_in, const float* const* s_in,
-                              const uint16_t* const* local, int8_t* const* q_out,
-                              float* const* s_out, int64_t n, hipStream_t stream);
+hipError_t launch_dequant(int count, const int8_t* const* q, const float* const* s,
+                          uint16_t* const* y, int64_t n, hipStream_t stream,
+                          int64_t skip_shard_n = 0);
+hipError_t launch_dequant(int count, const uint8_t* const* v, const uint8_t* const* e,
+                          uint16_t* const* y, int64_t n, hipStream_t stream,
+                          int64_t skip_shard_n = 0);
+hipError_t launch_ring_hop(int count, const int8_t* const* q_in, const float* const* s_in,
+                           const uint16_t* const* local, int8_t* const* q_out,
+                           float* const* s_out, int64_t n, hipStream_t stream);
+hipError_t launch_ring_hop(int count, const uint8_t* const* v_in, const uint8_t* const* e_in,
+                           const uint16_t* const* local, uint8_t* const* v_out,
+                           uint8_t* const* e_out, int64_t n, hipStream_t stream);
 // nseg segments of seg_n values: segment j reads q[k] + j*seg_n (scales likewise) for
 // every source k in order and writes y + j*seg_n.
-hipError_t launch_accum_i8(int nsrc, const int8_t* const* q, const float* const* s,
-                           uint16_t* y, int nseg, int64_t seg_n, hipStream_t stream);
+hipError_t launch_accum(int nsrc, const int8_t* const* q, const float* const* s, uint16_t* y,
+                        int nseg, int64_t seg_n, hipStream_t stream);
+hipError_t launch_accum(int nsrc, const uint8_t* const* v, const uint8_t* const* e, uint16_t* y,
+                        int nseg, int64_t seg_n, hipStream_t stream);
 // The fused all-to-all owner step: accumulate as above, requantize each owner's bf16
 // sum into q_out/s_out (segment j at j*seg_n), materialize it into y[j] (y or y[j] may
 // be null) and store the bf16 sums into red (may be null).
-hipError_t launch_a2a_reduce_i8(int nsrc, const int8_t* const* q, const float* const* s,
-                                int nseg, int64_t seg_n, int8_t* q_out, float* s_out,
-                                uint16_t* const* y, uint16_t* red, hipStream_t stream);
+hipError_t launch_a2a_reduce(int nsrc, const int8_t* const* q, const float* const* s, int nseg,
+                             int64_t seg_n, int8_t* q_out, float* s_out, uint16_t* const* y,
+                             uint16_t* red, hipStream_t stream);
+hipError_t launch_a2a_reduce(int nsrc, const uint8_t* const* v, const uint8_t* const* e,
+                             int nseg, int64_t seg_n, uint8_t* v_out, uint8_t* e_out,
+                             uint16_t* const* y, uint16_t* red, hipStream_t stream);
 
 // MXFP8 (row-major with leading dimensions; cols a multiple of 128).
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,

@@ -135,8 +135,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_mx(MxArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // 2^(byte-127): a normal binary32 for byte >= 1, the subnormal 2^-127 for byte 0
-            const float sc = __uint_as_float(ev[u] ? (ev[u] << 23) : 0x00400000u);
+            const float sc = e8m0_value(ev[u]);
             float f[8];
             e4m3_decode4(vv[u].x, f);
             e4m3_decode4(vv[u].y, f + 4);

@@ -27,7 +27,8 @@
  *     reaches the work.  No call synchronizes, so calls may be captured in a HIP graph.
  *   - Errors: every argument is validated on the host before anything is launched; on
  *     an error the call returns a status, writes nothing and launches nothing.
- *     BQ_ERR_LAUNCH reports a failure of the launch itself (hipGetLastError).
+ *     BQ_ERR_LAUNCH reports a failure of the launch itself (the status hipLaunchKernel
+ *     returns for that launch).
  *   - Alignment: bf16 and payload pointers 16-byte aligned; float scale arrays 4-byte
  *     aligned; E8M0 scale arrays 4-byte aligned with a row stride divisible by 4.
  *   - Aliasing: outputs must not overlap inputs or each other, except where an entry
@@ -198,6 +199,69 @@ bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64
  * total_cols must be a multiple of 128.  Host pointers. */
 bq_status bq_mx_staging_bytes(int64_t capacity_rows, int64_t total_cols, int64_t* value_bytes,
                               int64_t* scale_bytes);
+
+/* ==== MXFP8 on the collective topologies (P2 PR body Summary / Modes: mx_ring, mx_a2a) ====
+ *
+ * Flat layout of an MXFP8 wire payload of n values: v = u8[n] E4M3FN codes and
+ * e8m0 = u8[n/32], byte g scaling values [32g, 32g+32) -- 132 bytes per 128 values, the
+ * same spans as a block-INT8 payload.  A flat tensor quantizes and dequantizes with the
+ * bq_quant_mx / bq_dequant_mx rules (rows = 1, cols = n).  The collectives below are
+ * the INT8 ones with this codec, and carry the same canonical-payload rule: every rank,
+ * the owner included, materializes from the payload that is forwarded. */
+
+/* Batched flat quantize / dequantize: `count` (1..BQ_MAX_BATCH) segments of n values, one
+ * launch; segment i is bq_quant_mx / bq_dequant_mx of x[i] / (v[i], e8m0[i]) with rows = 1.
+ * Host arrays of device pointers.  v: 16-byte aligned; e8m0: 4-byte aligned. */
+bq_status bq_quant_mx_batch(int count, const uint16_t* const* x, int64_t n, uint8_t* const* v,
+                            uint8_t* const* e8m0, void* stream);
+bq_status bq_dequant_mx_batch(int count, const uint8_t* const* v, const uint8_t* const* e8m0,
+                              int64_t n, uint16_t* const* y, void* stream);
+
+/* One fused mx_ring hop: per value sum = fl32(fl32(e4m3(v_in) * 2^(byte-127)) + local)
+ * in binary32, then the binary32 sums of each 32-value group are requantized with the
+ * MXFP8 rule (byte from the group's binary32 amax: 127 + the smallest e with 2^e >=
+ * fl32(amax/448), clamped to [-127, 127], 0 when that quotient underflows; no bf16
+ * intermediate).  In place is allowed when v_out == v_in AND e_out == e_in exactly. */
+bq_status bq_ring_hop_mx(const uint8_t* v_in, const uint8_t* e_in, const uint16_t* local,
+                         int64_t n, uint8_t* v_out, uint8_t* e_out, void* stream);
+bq_status bq_ring_hop_mx_batch(int count, const uint8_t* const* v_in,
+                               const uint8_t* const* e_in, const uint16_t* const* local,
+                               int64_t n, uint8_t* const* v_out, uint8_t* const* e_out,
+                               void* stream);
+
+/* mx_a2a owner accumulate: acc = +0; for s = 0 .. nsrc-1 in that order acc = acc +
+ * e4m3(v_s) * 2^(byte_s - 127) (each term exact in binary32); y = bf16_rne(acc).
+ * 1 <= nsrc <= BQ_MAX_SRC. */
+bq_status bq_dequant_accum_mx(int nsrc, const uint8_t* const* v_srcs,
+                              const uint8_t* const* e_srcs, int64_t n, uint16_t* y,
+                              void* stream);
+
+/* Fused mx_a2a owner step, bit-identical to bq_dequant_accum_mx -> bq_quant_mx ->
+ * bq_dequant_mx on each owner's shard.  Arguments as bq_a2a_reduce_i8, with v/e8m0 in
+ * place of q/scale (owner j's scale bytes start at e_out + j*seg_n/32). */
+bq_status bq_a2a_reduce_mx(int nseg, int nsrc, const uint8_t* const* v_srcs,
+                           const uint8_t* const* e_srcs, int64_t seg_n, uint8_t* v_out,
+                           uint8_t* e_out, uint16_t* const* y_out, uint16_t* red, void* stream);
+
+/* MXFP8 all-gather materialization; arguments as bq_allgather_dequant_i8. */
+bq_status bq_allgather_dequant_mx(int world, const uint8_t* v, const uint8_t* e8m0, int64_t n,
+                                  uint16_t* const* out, int skip_own, void* stream);
+
+/* mx_ring all-reduce: the i8_ring schedule with the MXFP8 codec.  v_wire: u8[n],
+ * e_wire: u8[n/32]; on return they hold every chunk's final payload (chunk c at value
+ * offset c*n/W, scale offset c*n/(32W)).  Other arguments as bq_ring_allreduce_i8. */
+bq_status bq_ring_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                               uint8_t* v_wire, uint8_t* e_wire, uint16_t* const* out,
+                               void* stream);
+
+/* mx_a2a all-reduce: the i8_a2a schedule with the MXFP8 codec (the owner requantizes
+ * its bf16 sum once).  v_send/e_send: host arrays of W device pointers (u8[n], u8[n/32]);
+ * v_bcast: u8[n]; e_bcast: u8[n/32]; red: bf16[n] or NULL.  Other arguments as
+ * bq_a2a_allreduce_i8. */
+bq_status bq_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* partials,
+                              uint8_t* const* v_send, uint8_t* const* e_send, uint16_t* red,
+                              uint8_t* v_bcast, uint8_t* e_bcast, uint16_t* const* out,
+                              void* stream);
 
 /* ==== E4M3 128-block codec: the format the INT8 codec replaces (P1 Summary, Why) ==== */
 

@@ -21,6 +21,14 @@ if _build.stale():
 
 import block_quantized_wire_amd as bq  # noqa: E402
 
+# Every call below passes fake device addresses and must fail validation.  Should a case
+# be wrong and validate, the call would launch; with a GPU present that launch would touch
+# the fake addresses, so the module only runs where no GPU is visible.
+import torch  # noqa: E402
+
+if torch.cuda.device_count() > 0:
+    pytest.skip("host-only ABI tests run where no GPU is visible", allow_module_level=True)
+
 L = bq.lib
 OK, NULL, SIZE, ALIGN, BOUNDS, NSRC, ALIAS = range(7)
 A = 1 << 32          # a 16-byte aligned fake device address
@@ -203,3 +211,58 @@ def test_mx_slice_errors():
     assert f(x, rows, cols, cols, 0, v, total, e, total // 32 - 4, rows, S) == BOUNDS
     assert f(x, rows, cols, cols, 0, v, total, e, total // 32, rows - 1, S) == BOUNDS  # capacity
     assert f(x, rows, cols, cols, 0, None, total, e, total // 32, rows, S) == NULL
+
+
+def test_mx_collective_errors():
+    """The flat MXFP8 collectives share the INT8 validation: payload 16-byte aligned,
+    E8M0 arrays 4-byte aligned and n/32 bytes long, the same counts and overlap rules."""
+    n = 1024
+    v, e, loc = A, A + 4096, A + 8192
+    h = L.bq_ring_hop_mx
+    assert h(v, e, loc, 100, v, e, S) == SIZE
+    assert h(None, e, loc, n, v, e, S) == NULL
+    assert h(v + 8, e, loc, n, A + 2 ** 20, A + 2 ** 21, S) == ALIGN         # payload
+    assert h(v, e + 2, loc, n, A + 2 ** 20, A + 2 ** 21, S) == ALIGN         # E8M0 bytes
+    assert h(v, e, loc, n, v, A + 2 ** 21, S) == ALIAS                       # half in place
+    assert h(v, e, loc, n, v + 16, e, S) == ALIAS                            # partial overlap
+    assert h(v, e, loc, n, A + 2 ** 20, e + 16, S) == ALIAS                  # e_out inside e_in (n/32 B)
+    assert h(v, e, loc, n, loc + 64, A + 2 ** 21, S) == ALIAS                # over the local partial
+    assert h(v, e, loc, 0, v, e, S) == OK
+    b = L.bq_ring_hop_mx_batch
+    assert b(0, arr(v), arr(e), arr(loc), n, arr(v), arr(e), S) == NSRC
+    assert b(17, arr(v), arr(e), arr(loc), n, arr(v), arr(e), S) == NSRC
+    qb = L.bq_quant_mx_batch
+    assert qb(1, arr(A), n, arr(A + 2 ** 20), arr(A + 2 ** 20 + 512), S) == ALIAS   # v over e
+    assert qb(1, arr(A), 100, arr(A + 2 ** 20), arr(A + 2 ** 21), S) == SIZE
+    db = L.bq_dequant_mx_batch
+    assert db(1, arr(v), arr(e), n, arr(e - 64), S) == ALIAS
+    vs, es = arr(A, A + 4096), arr(A + 8192, A + 8192 + 64)
+    acc = L.bq_dequant_accum_mx
+    assert acc(0, vs, es, n, A + 2 ** 20, S) == NSRC
+    assert acc(65, vs, es, n, A + 2 ** 20, S) == NSRC
+    assert acc(2, vs, es, n, A + 8, S) == ALIGN
+    assert acc(2, vs, es, n, A + 512, S) == ALIAS                 # y over source 0
+    r = L.bq_a2a_reduce_mx
+    vo, eo = A + 65536, A + 65536 + 8192
+    ys = arr(A + 2 ** 20, A + 2 ** 20 + 4096)
+    assert r(2, 2, vs, es, n, A + 16, eo, ys, None, S) == ALIAS               # v_out over a source
+    assert r(2, 2, vs, es, n, vo, eo + 2, ys, None, S) == ALIGN
+    assert r(2, 2, vs, es, n, vo, eo, arr(A + 2 ** 20, A + 2 ** 20 + 1024), None, S) == ALIAS
+    assert r(17, 2, vs, es, n, vo, eo, ys, None, S) == NSRC
+    g = L.bq_allgather_dequant_mx
+    outs = arr(A + 2 ** 22, A + 2 ** 22 + 8192)
+    assert g(2, v, e, 128 * 3, outs, 1, S) == SIZE
+    assert g(2, v, e, n, arr(A + 2 ** 22, A + 2 ** 22 + 1024), 1, S) == ALIAS
+    assert g(2, v, e, n, arr(e, A + 2 ** 23), 0, S) == ALIAS
+    parts = arr(A, A + 4096)
+    routs = arr(A + 2 ** 21, A + 2 ** 21 + 4096)
+    ra = L.bq_ring_allreduce_mx
+    assert ra(3, n, parts, A + 2 ** 22, A + 2 ** 23, routs, S) == SIZE      # n % (128*3)
+    assert ra(2, n, parts, A + 2 ** 22, A + 2 ** 22 + 512, routs, S) == ALIAS   # wire v over e
+    assert ra(2, n, parts, A + 2 ** 22, A + 2 ** 23 + 1, routs, S) == ALIGN
+    aa = L.bq_a2a_allreduce_mx
+    vsend, esend = arr(A + 2 ** 24, A + 2 ** 24 + 4096), arr(A + 2 ** 25, A + 2 ** 25 + 64)
+    assert aa(2, n, parts, vsend, esend, None, A + 2 ** 26, A + 2 ** 26 + 512, routs, S) == ALIAS
+    assert aa(2, n, parts, vsend, arr(A + 2 ** 25, A + 2 ** 25 + 2), None, A + 2 ** 26,
+              A + 2 ** 27, routs, S) == ALIGN
+    assert aa(0, n, parts, vsend, esend, None, A + 2 ** 26, A + 2 ** 27, routs, S) == NSRC
