@@ -52,6 +52,9 @@ _SIGS = {
     "orc_quant_mx": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
     "orc_dequant_mx": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64], None),
     "orc_quant_mx_slice": ([_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
+    "orc_f16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
+    "orc_quant_mx_f16": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
+    "orc_quant_mx_slice_f16": ([_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64], None),
     "orc_ring_hop_mx": ([_P, _P, _P, _I64, _P, _P], None),
     "orc_dequant_accum_mx": ([ctypes.c_int, _P, _P, _I64, _P], None),
     "orc_a2a_reduce_mx": ([ctypes.c_int, ctypes.c_int, _P, _P, _I64, _P, _P, _P, _P], None),
@@ -228,6 +231,33 @@ def quant_mx_slice(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray) ->
     assert e.shape[1] * 32 >= v.shape[1] and e.shape[0] == v.shape[0]
     lib().orc_quant_mx_slice(x.ctypes.data, rows, cols, cols, col_off, v.ctypes.data,
                              v.shape[1], e.ctypes.data, e.shape[1])
+
+
+def f16_to_f32(h: int) -> float:
+    return lib().orc_f16_to_f32(h)
+
+
+def quant_mx_f16(x: np.ndarray):
+    """x: (rows, cols) uint16 IEEE binary16 -> (values (rows, cols), e8m0 (rows, cols/32))."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    v = np.zeros((rows, cols), np.uint8)
+    e = np.zeros((rows, cols // 32), np.uint8)
+    lib().orc_quant_mx_f16(x.ctypes.data, rows, cols, cols, v.ctypes.data, cols, e.ctypes.data,
+                           cols // 32)
+    return v, e
+
+
+def quant_mx_slice_f16(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray) -> None:
+    """quant_mx_slice for a binary16 slice."""
+    x = _c(x, np.uint16)
+    assert v.dtype == np.uint8 and e.dtype == np.uint8
+    assert v.flags.c_contiguous and e.flags.c_contiguous
+    rows, cols = x.shape
+    assert rows <= v.shape[0] and col_off + cols <= v.shape[1]
+    assert e.shape[1] * 32 >= v.shape[1] and e.shape[0] == v.shape[0]
+    lib().orc_quant_mx_slice_f16(x.ctypes.data, rows, cols, cols, col_off, v.ctypes.data,
+                                 v.shape[1], e.ctypes.data, e.shape[1])
 
 
 # ---- MXFP8 on the collective topologies (flat: n E4M3 bytes, n/32 E8M0 bytes) ----

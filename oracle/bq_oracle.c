@@ -377,8 +377,24 @@ static float mx_value(uint8_t code, uint8_t byte) {
     return ldexpf(orc_e4m3_decode(code), (int)byte - 127);
 }
 
-void orc_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                  uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds) {
+/* IEEE binary16 -> binary32, exact: sign, 5-bit exponent with bias 15, 10-bit
+ * fraction; exponent 0 holds the subnormals fraction * 2^-24.  Infinities and NaNs
+ * (exponent 31) are outside the contract. */
+float orc_f16_to_f32(uint16_t h) {
+    int ex = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    if (ex == 0x1F) {
+        fprintf(stderr, "bq_oracle: non-finite binary16 input is outside the contract\n");
+        abort();
+    }
+    float mag = (ex == 0) ? ldexpf((float)man, -24) : ldexpf((float)(1024 + man), ex - 25);
+    return (h & 0x8000u) ? -mag : mag;
+}
+
+/* MXFP8 quantization of rows of 16-bit inputs decoded by `to_f32`. */
+static void quant_mx_rows(float (*to_f32)(uint16_t), const uint16_t* x, int64_t rows,
+                          int64_t cols, int64_t ldx, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                          int64_t lds) {
     if (cols % MXG != 0) {
         fprintf(stderr, "bq_oracle: MX cols must be a multiple of 32\n");
         abort();
@@ -388,10 +404,22 @@ void orc_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
         for (int64_t g = 0; g < cols / MXG; g++) {
             const uint16_t* xg = x + r * ldx + g * MXG;
             for (int i = 0; i < MXG; i++)
-                xf[i] = orc_bf16_to_f32(xg[i]);
+                xf[i] = to_f32(xg[i]);
             quant_group_mx(xf, v + r * ldv + g * MXG, e8m0 + r * lds + g);
         }
     }
+}
+
+void orc_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                  uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds) {
+    quant_mx_rows(orc_bf16_to_f32, x, rows, cols, ldx, v, ldv, e8m0, lds);
+}
+
+/* The same rule on IEEE binary16 input (P4 Behavior: the slice quantizer takes BF16 or
+ * FP16 feature slices); every binary16 value is exact in binary32. */
+void orc_quant_mx_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds) {
+    quant_mx_rows(orc_f16_to_f32, x, rows, cols, ldx, v, ldv, e8m0, lds);
 }
 
 /* y = bf16(fl32(e4m3 * 2^(byte-127))). */
@@ -418,6 +446,16 @@ void orc_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
         abort();
     }
     orc_quant_mx(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / MXG, lds);
+}
+
+void orc_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                            int64_t lds) {
+    if (col_off % 128 != 0 || cols % 128 != 0) {
+        fprintf(stderr, "bq_oracle: slices and offsets must be multiples of 128\n");
+        abort();
+    }
+    orc_quant_mx_f16(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / MXG, lds);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -77,6 +77,13 @@ void orc_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t 
 void orc_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                         int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
                         int64_t lds);
+/* IEEE binary16 input (P4 Behavior: BF16 or FP16 slices). */
+float orc_f16_to_f32(uint16_t h);
+void orc_quant_mx_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds);
+void orc_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                            int64_t lds);
 
 /* ---- MXFP8 on the collective topologies (P2 Summary / Modes) ----------
  * Flat layout: n E4M3 bytes and n/32 E8M0 bytes; group g = values [32g, 32g+32). */

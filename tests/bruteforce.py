@@ -183,3 +183,14 @@ def mx_accum_value(codes, bytes_) -> int:
     for c, b in zip(codes, bytes_):
         acc = rn32(acc + rn32(e4m3_value(c) * Fraction(2) ** (b - 127)))
     return fraction_to_bf16_bits(acc)
+
+
+def f16_bits_to_fraction(h: int) -> Fraction:
+    """Exact value of a finite IEEE binary16 bit pattern, decoded from its fields."""
+    sign = -1 if (h >> 15) & 1 else 1
+    ex = (h >> 10) & 0x1F
+    man = h & 0x3FF
+    assert ex != 0x1F, "non-finite"
+    if ex == 0:
+        return sign * Fraction(man) * Fraction(2) ** -24
+    return sign * Fraction(1024 + man) * Fraction(2) ** (ex - 25)

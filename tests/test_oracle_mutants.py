@@ -52,6 +52,10 @@ MUTANTS = [
     ("MX hop rounds the sums to bf16 first", "            sums[i] = dq + lp;",
      "            sums[i] = orc_bf16_to_f32(orc_f32_to_bf16(dq + lp));",
      ["test_mx_ring_hop_bruteforce_and_identities"]),
+    ("binary16 exponent bias off by one", "ldexpf((float)(1024 + man), ex - 25)",
+     "ldexpf((float)(1024 + man), ex - 24)", ["test_f16_decode_exhaustive_matches_numpy"]),
+    ("binary16 subnormal step 2^-23", "ldexpf((float)man, -24)", "ldexpf((float)man, -23)",
+     ["test_f16_decode_exhaustive_matches_numpy"]),
     ("A2A requantizes only the first shard", "for (int j = 0; j < W; j++) {\n        for (int s = 0; s < W; s++) {",
      "for (int j = 0; j < 1; j++) {\n        for (int s = 0; s < W; s++) {",
      ["test_a2a_requantizes_the_bf16_sum"]),

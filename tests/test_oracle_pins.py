@@ -724,3 +724,84 @@ def test_mx_a2a_allreduce_exact_sums(W):
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     assert np.array_equal(outs[0], oracle.dequant_mx_flat(vf, ef))
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP8 of binary16 slices (the staged quantizer takes BF16 or FP16 slices)
+# ---------------------------------------------------------------------------------------
+
+def all_finite_f16() -> np.ndarray:
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return h[((h >> 10) & 0x1F) != 0x1F]
+
+
+def test_f16_decode_exhaustive_matches_numpy():
+    h = all_finite_f16()
+    L = oracle.lib()
+    got = np.fromiter((L.orc_f16_to_f32(int(v)) for v in h), dtype=np.float32, count=h.size)
+    want = h.view(np.float16).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))     # signed zeros too
+    for v in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xFBFF):
+        assert Fraction(float(L.orc_f16_to_f32(v))) == bf.f16_bits_to_fraction(v)
+
+
+def test_e8m0_over_every_f16_amax():
+    """Smallest power of two >= fl32(amax/448) over every positive finite binary16 amax;
+    for amax = m 2^k it is k - 8 + [m > 1.75] (no clamping is reached from binary16)."""
+    h = all_finite_f16()
+    h = h[(h > 0) & (h < 0x8000)]
+    amax = h.view(np.float16).astype(np.float32)
+    d = (amax / np.float32(448.0)).astype(np.float64)
+    e = np.full(d.shape, 200, np.int64)
+    for k in range(127, -128, -1):
+        e = np.where(2.0 ** k >= d, k, e)
+    L = oracle.lib()
+    got = np.fromiter((L.orc_e8m0_scale(float(a)) for a in amax), dtype=np.uint8, count=amax.size)
+    assert np.array_equal(got.astype(np.int64) - 127, e)
+    m, k = np.frexp(amax.astype(np.float64))
+    assert np.array_equal(e, (k - 1) - 8 + (m * 2 > 1.75))
+
+
+def test_mx_f16_quant_bruteforce_rows():
+    x = workloads.rows(4, 0, 0, 3, 256, fmt="f16")   # per-row gains: subnormals to hundreds
+    v, e = oracle.quant_mx_f16(x)
+    for r in range(3):
+        for g in range(8):
+            grp = [bf.f16_bits_to_fraction(int(h)) for h in x[r, g * 32:(g + 1) * 32]]
+            byte = bf.e8m0_byte(max(abs(t) for t in grp))
+            assert e[r, g] == byte
+            sc = Fraction(2) ** (byte - 127)
+            for i, t in enumerate(grp):
+                neg0 = t == 0 and (x[r, g * 32 + i] & 0x8000) != 0
+                assert v[r, g * 32 + i] == bf.e4m3_nearest(bf.rn32(t / sc), negative_zero=neg0)
+
+
+def test_mx_f16_equals_bf16_on_values_both_formats_hold():
+    """A value with at most 8 significant bits in the binary16 normal range is the same
+    number in bf16; the MXFP8 quantization of the two encodings must agree."""
+    rng = np.random.default_rng(8)
+    sig = rng.integers(128, 256, (16, 512)).astype(np.float64)          # 8-bit significands
+    ex = rng.integers(-14 - 7, 15 - 7 + 1, (16, 512))
+    vals = sig * 2.0 ** ex * np.where(rng.random((16, 512)) < 0.5, -1, 1)
+    vals[:, ::37] = 0.0
+    h16 = vals.astype(np.float16)
+    assert np.array_equal(h16.astype(np.float64), vals)
+    b = vals.astype(np.float32).view(np.uint32)
+    assert not np.any(b & 0xFFFF)
+    v16, e16 = oracle.quant_mx_f16(h16.view(np.uint16))
+    vbf, ebf = oracle.quant_mx((b >> 16).astype(np.uint16))
+    assert np.array_equal(v16, vbf) and np.array_equal(e16, ebf)
+
+
+def test_mx_f16_slices_equal_concatenation_and_leave_the_rest_untouched():
+    R, C, S = 8, 256, 3
+    xs = [workloads.rows(4, j, 0, R, C, fmt="f16") for j in range(S)]
+    cat = np.concatenate(xs, axis=1)
+    wv, we = oracle.quant_mx_f16(cat)
+    cap = R + 3
+    v = np.full((cap, S * C), 0xA5, np.uint8)
+    e = np.full((cap, S * C // 32), 0x5A, np.uint8)
+    for j in (2, 0, 1):
+        oracle.quant_mx_slice_f16(xs[j], j * C, v, e)
+    assert np.array_equal(v[:R], wv) and np.array_equal(e[:R], we)
+    assert np.all(v[R:] == 0xA5) and np.all(e[R:] == 0x5A)

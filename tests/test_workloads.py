@@ -65,3 +65,17 @@ def test_truncation_not_rounding():
     # the generator truncates binary32 to bf16; it must never produce NaN or inf
     x = workloads.rows(5, 2, 0, 64, 7168)
     assert np.all(((x >> 7) & 0xFF) != 0xFF)
+
+
+def test_f16_mode_truncates_the_same_draws():
+    """The binary16 mode draws the same doubles as the bf16 mode and truncates them toward
+    zero: signs agree, and the two truncations of one value differ by less than a bf16
+    ulp plus a binary16 subnormal step."""
+    a = workloads.rows(4, 3, 0, 32, 1024, fmt="f16")
+    b = workloads.rows(4, 3, 0, 32, 1024)
+    fa = a.view(np.float16).astype(np.float64)
+    fb = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.isfinite(fa))
+    assert np.all((fa == 0) | (fb == 0) | (np.sign(fa) == np.sign(fb)))
+    assert np.all(np.abs(fa - fb) <= np.abs(fb) * 2.0 ** -7 + 2.0 ** -24)
+    assert np.array_equal(workloads.rows(4, 3, 5, 2, 1024, fmt="f16"), a[5:7])

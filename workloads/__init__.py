@@ -50,6 +50,9 @@ def _load():
         lib.bqgen_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
         lib.bqgen_rows.restype = None
+        lib.bqgen_rows_fmt.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.bqgen_rows_fmt.restype = None
         lib.bqgen_shape.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                     ctypes.POINTER(ctypes.c_int64)]
         lib.bqgen_shape.restype = ctypes.c_int
@@ -74,8 +77,9 @@ def shape(cfg: int) -> tuple[int, int]:
 
 
 def rows(cfg: int, rank: int, row0: int, nrows: int, cols: int | None = None,
-         out: np.ndarray | None = None) -> np.ndarray:
-    """bf16 bit patterns (uint16) of rows [row0, row0+nrows) of rank's tensor."""
+         out: np.ndarray | None = None, fmt: str = "bf16") -> np.ndarray:
+    """bf16 (or, with fmt="f16", IEEE binary16) bit patterns (uint16) of rows
+    [row0, row0+nrows) of rank's tensor."""
     if cols is None:
         cols = shape(cfg)[1]
     if cols % 128 != 0:
@@ -83,7 +87,10 @@ def rows(cfg: int, rank: int, row0: int, nrows: int, cols: int | None = None,
     if out is None:
         out = np.empty((nrows, cols), dtype=np.uint16)
     assert out.dtype == np.uint16 and out.flags.c_contiguous and out.size == nrows * cols
-    _load().bqgen_rows(cfg, rank, row0, nrows, cols, out.ctypes.data, threads())
+    if fmt not in ("bf16", "f16"):
+        raise ValueError(f"unknown format {fmt}")
+    _load().bqgen_rows_fmt(cfg, rank, row0, nrows, cols, out.ctypes.data, threads(),
+                           1 if fmt == "f16" else 0)
     return out
 
 

@@ -15,9 +15,11 @@
  * Every (config, rank, stream kind, row) has its own stream, so any row of
  * any rank can be regenerated on its own, in any order and on any number of
  * threads, with identical results.  Values are drawn in double, cast to
- * binary32 and then TRUNCATED to bf16 (the top 16 bits).  Truncation is a
- * deliberate choice: the codecs round to nearest-even, and the generator
- * shares no rounding code with them.
+ * binary32 and then TRUNCATED to bf16 (the top 16 bits), or -- for the FP16
+ * slice inputs -- truncated toward zero to IEEE binary16 from the double,
+ * saturating at the binary16 maximum 65504 and keeping binary16 subnormals.
+ * Truncation is a deliberate choice: the codecs round to nearest-even, and
+ * the generator shares no rounding code with them.
  *
  * Build: cc -std=c99 -O2 -fopenmp -fPIC -shared -lm
  */
@@ -101,6 +103,23 @@ static uint16_t to_bf16_trunc(double d) {
     return (uint16_t)(u >> 16);
 }
 
+/* binary16 bits of d truncated toward zero (finite d). */
+static uint16_t to_f16_trunc(double d) {
+    uint16_t sign = signbit(d) ? 0x8000u : 0u;
+    double a = fabs(d);
+    if (a >= 65504.0)
+        return sign | 0x7BFFu;
+    if (a < 0x1.0p-14)                                   /* subnormal: multiples of 2^-24 */
+        return sign | (uint16_t)floor(a * 0x1.0p24);
+    int e;
+    double m = frexp(a, &e);                             /* a = m 2^e, m in [0.5, 1) */
+    uint16_t man = (uint16_t)floor((m * 2.0 - 1.0) * 1024.0);
+    return sign | (uint16_t)((e - 1 + 15) << 10) | man;
+}
+
+/* output format of a generated value: 0 = bf16 (truncated), 1 = binary16 (truncated) */
+static uint16_t enc(double d, int fmt) { return fmt == 1 ? to_f16_trunc(d) : to_bf16_trunc(d); }
+
 /*
  * Config table.  Shapes are rows x cols of one rank's (or slice's) tensor.
  *   1: 512x7168, N(0,1); each element x50 with prob 1e-3; each 128-block
@@ -126,7 +145,7 @@ int bqgen_shape(int cfg, int64_t* rows, int64_t* cols) {
     }
 }
 
-static void gen_row(int cfg, int rank, int64_t row, int64_t cols, uint16_t* out) {
+static void gen_row(int cfg, int rank, int64_t row, int64_t cols, uint16_t* out, int fmt) {
     rng_t rv, ro, rz, rs, rg, rsg;
     rng_init(&rv, cfg, rank, K_VALUE, row);
     switch (cfg) {
@@ -139,26 +158,26 @@ static void gen_row(int cfg, int rank, int64_t row, int64_t cols, uint16_t* out)
                 double v = normal(&rv);
                 if (uniform(&ro) <= 1e-3)
                     v *= 50.0;
-                out[i] = zero ? 0 : to_bf16_trunc(v);
+                out[i] = zero ? 0 : enc(v, fmt);
             }
         }
         break;
     }
     case 2:
         for (int64_t i = 0; i < cols; i++)
-            out[i] = to_bf16_trunc(0.5 * normal(&rv));
+            out[i] = enc(0.5 * normal(&rv), fmt);
         break;
     case 3:
     case 7:
         for (int64_t i = 0; i < cols; i++)
-            out[i] = to_bf16_trunc(0.3 * student_t(&rv, 4));
+            out[i] = enc(0.3 * student_t(&rv, 4), fmt);
         break;
     case 4: {
         rng_init(&rg, cfg, rank, K_GAIN, row);
         double lg = log(1e-3) + (log(1e2) - log(1e-3)) * uniform(&rg);
         double g = exp(lg);
         for (int64_t i = 0; i < cols; i++)
-            out[i] = to_bf16_trunc(g * normal(&rv));
+            out[i] = enc(g * normal(&rv), fmt);
         break;
     }
     case 5: {
@@ -171,28 +190,34 @@ static void gen_row(int cfg, int rank, int64_t row, int64_t cols, uint16_t* out)
                 double v = student_t(&rv, 3);
                 if (uniform(&rs) <= 1e-5)
                     v = (uniform(&rsg) <= 0.5) ? 1e3 : -1e3;
-                out[i] = zero ? 0 : to_bf16_trunc(v);
+                out[i] = zero ? 0 : enc(v, fmt);
             }
         }
         break;
     }
     default: /* 6 */
         for (int64_t i = 0; i < cols; i++)
-            out[i] = to_bf16_trunc(normal(&rv));
+            out[i] = enc(normal(&rv), fmt);
         break;
     }
 }
 
 /* Rows [row0, row0+nrows) of `rank`'s tensor for config `cfg`, cols values
- * per row (cols a multiple of 128), written densely to out. */
-void bqgen_rows(int cfg, int rank, int64_t row0, int64_t nrows, int64_t cols, uint16_t* out,
-                int nthreads) {
+ * per row (cols a multiple of 128), written densely to out in format fmt
+ * (0 = bf16, 1 = binary16). */
+void bqgen_rows_fmt(int cfg, int rank, int64_t row0, int64_t nrows, int64_t cols, uint16_t* out,
+                    int nthreads, int fmt) {
 #ifdef _OPENMP
     if (nthreads < 1)
         nthreads = 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
 #endif
     for (int64_t r = 0; r < nrows; r++)
-        gen_row(cfg, rank, row0 + r, cols, out + r * cols);
+        gen_row(cfg, rank, row0 + r, cols, out + r * cols, fmt);
     (void)nthreads;
+}
+
+void bqgen_rows(int cfg, int rank, int64_t row0, int64_t nrows, int64_t cols, uint16_t* out,
+                int nthreads) {
+    bqgen_rows_fmt(cfg, rank, row0, nrows, cols, out, nthreads, 0);
 }
