@@ -24,6 +24,7 @@ __all__ = [
     "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
     "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
     "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
+    "bq_quant_mx_f16", "bq_quant_mx_slice_f16",
     "bq_quant_mx_batch", "bq_dequant_mx_batch", "bq_ring_hop_mx", "bq_ring_hop_mx_batch",
     "bq_dequant_accum_mx", "bq_a2a_reduce_mx", "bq_allgather_dequant_mx",
     "bq_ring_allreduce_mx", "bq_a2a_allreduce_mx",
@@ -64,6 +65,8 @@ _SIGS = {
     "bq_dequant_mx": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
     "bq_quant_mx_slice": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
     "bq_mx_staging_bytes": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "bq_quant_mx_f16": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
+    "bq_quant_mx_slice_f16": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
     "bq_quant_mx_batch": [_I, _PP, _I64, _PP, _PP, _P],
     "bq_dequant_mx_batch": [_I, _PP, _PP, _I64, _PP, _P],
     "bq_ring_hop_mx": [_P, _P, _P, _I64, _P, _P, _P],
@@ -269,6 +272,35 @@ def bq_quant_mx_slice(x, col_off: int, v, e8m0, capacity_rows: int | None = None
     _check("bq_quant_mx_slice",
            _L().bq_quant_mx_slice(_ptr(x), rows, cols, ldx, col_off, _ptr(v), ldv, _ptr(e8m0), lds,
                                  capacity_rows, _stream(stream)))
+
+
+def bq_quant_mx_f16(x, v, e8m0, rows: int | None = None, cols: int | None = None,
+                    ldx: int | None = None, ldv: int | None = None, lds: int | None = None,
+                    stream=None) -> None:
+    """bq_quant_mx on IEEE binary16 input (x: torch.float16 or int16 bit views)."""
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ldx = x.stride(0) if ldx is None else ldx
+    ldv = v.stride(0) if ldv is None else ldv
+    lds = e8m0.stride(0) if lds is None else lds
+    _check("bq_quant_mx_f16", _L().bq_quant_mx_f16(_ptr(x), rows, cols, ldx, _ptr(v), ldv,
+                                                  _ptr(e8m0), lds, _stream(stream)))
+
+
+def bq_quant_mx_slice_f16(x, col_off: int, v, e8m0, capacity_rows: int | None = None,
+                          rows: int | None = None, cols: int | None = None,
+                          ldx: int | None = None, ldv: int | None = None, lds: int | None = None,
+                          stream=None) -> None:
+    """bq_quant_mx_slice on an IEEE binary16 slice."""
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ldx = x.stride(0) if ldx is None else ldx
+    ldv = v.stride(0) if ldv is None else ldv
+    lds = e8m0.stride(0) if lds is None else lds
+    capacity_rows = v.shape[0] if capacity_rows is None else capacity_rows
+    _check("bq_quant_mx_slice_f16",
+           _L().bq_quant_mx_slice_f16(_ptr(x), rows, cols, ldx, col_off, _ptr(v), ldv, _ptr(e8m0),
+                                     lds, capacity_rows, _stream(stream)))
 
 
 def bq_mx_staging_bytes(capacity_rows: int, total_cols: int) -> tuple[int, int]:

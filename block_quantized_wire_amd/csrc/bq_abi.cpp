@@ -586,8 +586,10 @@ int64_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
 
 }  // namespace
 
-bq_status bq_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* v,
-                      int64_t ldv, uint8_t* e8m0, int64_t lds, void* stream) {
+namespace {
+
+bq_status quant_mx_2d(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* v,
+                      int64_t ldv, uint8_t* e8m0, int64_t lds, bool f16, void* stream) {
     BQ_TRY(check_mx_shape(rows, cols));
     if (rows == 0 || cols == 0)
         return BQ_OK;
@@ -603,12 +605,13 @@ bq_status bq_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
     const Span es = span(e8m0, extent(rows, cols / BQ_MX_GROUP, lds, 1));
     if (overlaps(xs, vs) || overlaps(xs, es) || overlaps(vs, es))
         return BQ_ERR_ALIAS;
-    return launched(bq::launch_quant_mx(x, rows, cols, ldx, v, ldv, e8m0, lds, as_stream(stream)));
+    return launched(
+        bq::launch_quant_mx(x, rows, cols, ldx, v, ldv, e8m0, lds, as_stream(stream), f16));
 }
 
-bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                            int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
-                            int64_t lds, int64_t capacity_rows, void* stream) {
+bq_status quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                         int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds,
+                         int64_t capacity_rows, bool f16, void* stream) {
     BQ_TRY(check_mx_shape(rows, cols));
     if (col_off < 0 || col_off % kBlk != 0 || ldv < 0 || ldv % kBlk != 0)
         return BQ_ERR_SIZE;
@@ -618,8 +621,34 @@ bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64
         return BQ_OK;
     if (!x || !v || !e8m0)
         return BQ_ERR_NULL;
-    return bq_quant_mx(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / BQ_MX_GROUP, lds,
-                       stream);
+    return quant_mx_2d(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / BQ_MX_GROUP, lds,
+                       f16, stream);
+}
+
+}  // namespace
+
+bq_status bq_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* v,
+                      int64_t ldv, uint8_t* e8m0, int64_t lds, void* stream) {
+    return quant_mx_2d(x, rows, cols, ldx, v, ldv, e8m0, lds, false, stream);
+}
+
+bq_status bq_quant_mx_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds, void* stream) {
+    return quant_mx_2d(x, rows, cols, ldx, v, ldv, e8m0, lds, true, stream);
+}
+
+bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                            int64_t lds, int64_t capacity_rows, void* stream) {
+    return quant_mx_slice(x, rows, cols, ldx, col_off, v, ldv, e8m0, lds, capacity_rows, false,
+                          stream);
+}
+
+bq_status bq_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                                int64_t lds, int64_t capacity_rows, void* stream) {
+    return quant_mx_slice(x, rows, cols, ldx, col_off, v, ldv, e8m0, lds, capacity_rows, true,
+                          stream);
 }
 
 bq_status bq_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,

@@ -95,6 +95,19 @@ __device__ __forceinline__ void unpack_bf16x8(u32x4 w, float f[8]) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// The 8 IEEE binary16 values of a 16-byte vector as binary32 (v_cvt_f32_f16 is exact,
+// subnormals included: denormals are not flushed in this library).
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack_f16x8(u32x4 w, float f[8]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h16x2 h = __builtin_bit_cast(h16x2, ws[i]);
+        f[2 * i] = (float)h.x;
+        f[2 * i + 1] = (float)h.y;
+    }
+}
+
 // Round two binary32 values to bf16 (nearest, ties to even) and pack them, a in the
 // low half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

@@ -58,9 +58,10 @@ hipError_t launch_a2a_reduce(int nsrc, const uint8_t* const* v, const uint8_t* c
                              uint16_t* const* y, uint16_t* red, hipStream_t stream);
 
 // MXFP8 (row-major with leading dimensions; cols a multiple of 128).
+// f16: x holds IEEE binary16 values instead of bf16.
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds,
-                           hipStream_t stream);
+                           hipStream_t stream, bool f16 = false);
 hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
                              int64_t rows, int64_t cols, uint16_t* y, int64_t ldy,
                              hipStream_t stream);

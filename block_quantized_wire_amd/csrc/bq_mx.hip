@@ -77,7 +77,9 @@ struct Walk {
     }
 };
 
-template <int U>
+// F16: the input is IEEE binary16 (b12x pull request #241, Behavior: BF16 or FP16 slices);
+// the group byte then comes from the binary32 amax rule, which is exact for any amax.
+template <int U, bool F16>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
     const Walk w(U);
     const int lane = threadIdx.x & 63;
@@ -93,13 +95,17 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float f[8];
-            unpack_bf16x8(xv[u], f);
+            if constexpr (F16)
+                unpack_f16x8(xv[u], f);
+            else
+                unpack_bf16x8(xv[u], f);
             float m = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
             const uint32_t amax_bits = quad_max4(__float_as_uint(m));
-            const uint32_t byte = e8m0_from_bf16_amax(amax_bits >> 16);
+            const uint32_t byte = F16 ? e8m0_from_f32_amax(__uint_as_float(amax_bits))
+                                      : e8m0_from_bf16_amax(amax_bits >> 16);
             const float inv = e8m0_inv_scale(byte);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -240,7 +246,7 @@ constexpr int kUE4 = 2;
 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool f16) {
     MxArgs a{};
     a.x = x;
     a.v = v;
@@ -250,7 +256,10 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
     a.lds = lds;
     a.nblocks = (uint32_t)(rows * (cols / kBlock));
     a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
-    return launch1(k_quant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads), stream, a);
+    const dim3 grid(groups_for<kUMx>(a.nblocks));
+    if (f16)
+        return launch1(k_quant_mx<kUMx, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_mx<kUMx, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,

@@ -194,6 +194,16 @@ bq_status bq_quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64
                             int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
                             int64_t lds, int64_t capacity_rows, void* stream);
 
+/* The same two calls on IEEE binary16 input (P4 Behavior: the slice quantizer takes BF16
+ * or FP16 slices).  x holds binary16 bit patterns (finite); every binary16 value is exact
+ * in binary32, and the group byte follows the rule above from that binary32 amax.
+ * Arguments, layout and errors as bq_quant_mx / bq_quant_mx_slice. */
+bq_status bq_quant_mx_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t* v, int64_t ldv, uint8_t* e8m0, int64_t lds, void* stream);
+bq_status bq_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
+                                int64_t lds, int64_t capacity_rows, void* stream);
+
 /* Sizes of a staging buffer for `capacity_rows` rows of `total_cols` columns (the
  * allocation helper of P4 Behavior, as a host-side size query: the caller allocates).
  * total_cols must be a multiple of 128.  Host pointers. */

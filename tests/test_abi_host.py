@@ -266,3 +266,16 @@ def test_mx_collective_errors():
     assert aa(2, n, parts, vsend, arr(A + 2 ** 25, A + 2 ** 25 + 2), None, A + 2 ** 26,
               A + 2 ** 27, routs, S) == ALIGN
     assert aa(0, n, parts, vsend, esend, None, A + 2 ** 26, A + 2 ** 27, routs, S) == NSRC
+
+
+def test_mx_f16_errors():
+    rows, cols = 16, 512
+    x, v, e = A, A + 2 ** 20, A + 2 ** 21
+    assert L.bq_quant_mx_f16(x, rows, 100, 512, v, 512, e, 16, S) == SIZE
+    assert L.bq_quant_mx_f16(x, rows, cols, 512, v, 512, e + 2, 16, S) == ALIGN
+    assert L.bq_quant_mx_f16(x, rows, cols, 512, x + 1024, 512, e, 16, S) == ALIAS
+    assert L.bq_quant_mx_f16(x, 0, cols, 512, v, 512, e, 16, S) == OK
+    f = L.bq_quant_mx_slice_f16
+    assert f(x, rows, cols, 512, 64, v, 2048, e, 64, rows, S) == SIZE          # offset % 128
+    assert f(x, rows, cols, 512, 1664, v, 2048, e, 64, rows, S) == BOUNDS      # past ldv
+    assert f(x, rows, cols, 512, 0, v, 2048, e, 64, rows - 1, S) == BOUNDS     # capacity
