@@ -260,6 +260,30 @@ def quant_mx_slice_f16(x: np.ndarray, col_off: int, v: np.ndarray, e: np.ndarray
                                  v.shape[1], e.ctypes.data, e.shape[1])
 
 
+# ---- the MXFP8 GEMM from staged inputs (b12x PR #241, Behavior: mm_quantized) ----------
+
+def mx_values_f64(v: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """Exact values of an MXFP8 matrix (rows, cols) in float64: each E4M3 code (decoded by
+    orc_e4m3_decode) times 2^(byte - 127) of its 32-column group."""
+    v = _c(v, np.uint8)
+    e = _c(e, np.uint8)
+    rows, cols = v.shape
+    assert e.shape[0] == rows and e.shape[1] * 32 >= cols
+    table = np.array([lib().orc_e4m3_decode(c) for c in range(256)], np.float64)
+    scale = np.ldexp(1.0, np.repeat(e[:, :cols // 32].astype(np.int64) - 127, 32, axis=1))
+    return table[v] * scale
+
+
+def mm_mx(xv: np.ndarray, xe: np.ndarray, wv: np.ndarray, we: np.ndarray):
+    """The dense GEMM of MXFP8 activations X (M, K) and weights W (N, K): returns
+    (Y, S) with Y = X W^T and S = |X| |W|^T, both float64 from the exact operand values
+    (every product is exact in float64; a float64 matmul is the one library step)."""
+    X = mx_values_f64(xv, xe)
+    Wt = mx_values_f64(wv, we)
+    assert X.shape[1] == Wt.shape[1]
+    return X @ Wt.T, np.abs(X) @ np.abs(Wt).T
+
+
 # ---- MXFP8 on the collective topologies (flat: n E4M3 bytes, n/32 E8M0 bytes) ----
 
 def quant_mx_flat(x: np.ndarray):

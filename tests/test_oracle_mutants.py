@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -94,3 +95,43 @@ def test_pins_catch_planted_mistake(mutant_lib, desc, old, new, tests, tmp_path)
             kwargs["W"] = 4
         with pytest.raises(AssertionError):
             fn(**kwargs)
+
+
+def _mm_with_values(values_fn):
+    def mm(xv, xe, wv, we):
+        X, Wt = values_fn(xv, xe), values_fn(wv, we)
+        return X @ Wt.T, np.abs(X) @ np.abs(Wt).T
+    return mm
+
+
+def _values_exponent_off_by_one(v, e):
+    table = np.array([oracle.lib().orc_e4m3_decode(c) for c in range(256)], np.float64)
+    return table[v] * np.ldexp(1.0, np.repeat(e.astype(np.int64) - 126, 32, axis=1))[:, :v.shape[1]]
+
+
+def _values_group_of_64(v, e):
+    table = np.array([oracle.lib().orc_e4m3_decode(c) for c in range(256)], np.float64)
+    return table[v] * np.ldexp(1.0, np.repeat(e[:, ::2].astype(np.int64) - 127, 64, axis=1))
+
+
+def _mm_sums_magnitudes(xv, xe, wv, we):
+    X, Wt = oracle.mx_values_f64(xv, xe), oracle.mx_values_f64(wv, we)
+    return np.abs(X) @ np.abs(Wt).T, np.abs(X) @ np.abs(Wt).T
+
+
+PY_MUTANTS = [
+    ("GEMM scale exponent off by one", _mm_with_values(_values_exponent_off_by_one),
+     ["test_mm_mx_worked_cases", "test_mm_mx_bruteforce_tiny"]),
+    ("GEMM scale groups of 64 columns", _mm_with_values(_values_group_of_64),
+     ["test_mm_mx_worked_cases", "test_mm_mx_bruteforce_tiny"]),
+    ("GEMM drops the signs", _mm_sums_magnitudes,
+     ["test_mm_mx_worked_cases", "test_mm_mx_bruteforce_tiny"]),
+]
+
+
+@pytest.mark.parametrize("desc,fn,tests", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_planted_python_mistake(monkeypatch, desc, fn, tests):
+    monkeypatch.setattr(oracle, "mm_mx", fn)
+    for name in tests:
+        with pytest.raises(AssertionError):
+            getattr(pins, name)()

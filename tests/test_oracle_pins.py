@@ -805,3 +805,58 @@ def test_mx_f16_slices_equal_concatenation_and_leave_the_rest_untouched():
         oracle.quant_mx_slice_f16(xs[j], j * C, v, e)
     assert np.array_equal(v[:R], wv) and np.array_equal(e[:R], we)
     assert np.all(v[R:] == 0xA5) and np.all(e[R:] == 0x5A)
+
+
+# ---------------------------------------------------------------------------------------
+# the MXFP8 GEMM from staged inputs (the plain definition: Y = X W^T on exact values)
+# ---------------------------------------------------------------------------------------
+
+def test_mm_mx_worked_cases():
+    """All-ones codes: each output is the sum over groups of 32 * 2^(ex + ew - 254)."""
+    M, N, K = 3, 5, 256
+    xv = np.full((M, K), 0x38, np.uint8)
+    wv = np.full((N, K), 0x38, np.uint8)
+    xe = np.full((M, K // 32), 127, np.uint8)
+    we = np.full((N, K // 32), 127, np.uint8)
+    xe[1, 2], we[4, 2], xe[2, 7] = 130, 120, 0
+    Y, S = oracle.mm_mx(xv, xe, wv, we)
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            want[m, n] = sum(32 * 2.0 ** (int(xe[m, g]) + int(we[n, g]) - 254) for g in range(K // 32))
+    assert np.array_equal(Y, want) and np.array_equal(S, want)
+    xv[0, :] = 0xB8                                                  # -1.0
+    Y, S = oracle.mm_mx(xv, xe, wv, we)
+    assert np.array_equal(Y[0], -want[0]) and np.array_equal(S[0], want[0])
+
+
+def test_mm_mx_bruteforce_tiny():
+    x = workloads.rows(4, 0, 0, 3, 128)
+    w = workloads.rows(7, 1, 0, 2, 128)
+    xv, xe = oracle.quant_mx(x)
+    wv, we = oracle.quant_mx(w)
+    Y, S = oracle.mm_mx(xv, xe, wv, we)
+    for m in range(3):
+        for n in range(2):
+            acc = Fraction(0)
+            acs = Fraction(0)
+            for k in range(128):
+                a = bf.e4m3_value(int(xv[m, k])) * Fraction(2) ** (int(xe[m, k // 32]) - 127)
+                b = bf.e4m3_value(int(wv[n, k])) * Fraction(2) ** (int(we[n, k // 32]) - 127)
+                acc += a * b
+                acs += abs(a * b)
+            assert Fraction(Y[m, n]) == acc and Fraction(S[m, n]) == acs
+
+
+def test_mm_mx_matches_the_pinned_dequantize():
+    """Where the bf16 materialization is exact (no value below 2^-133), the GEMM of the
+    materialized operands is the same number."""
+    x = workloads.rows(6, 2, 0, 8, 512)
+    w = workloads.rows(7, 3, 0, 6, 512)
+    xv, xe = oracle.quant_mx(x)
+    wv, we = oracle.quant_mx(w)
+    Y, _ = oracle.mm_mx(xv, xe, wv, we)
+    xd = f32(oracle.dequant_mx(xv, xe)).astype(np.float64)
+    wd = f32(oracle.dequant_mx(wv, we)).astype(np.float64)
+    assert np.array_equal(oracle.mx_values_f64(xv, xe), xd)
+    assert np.allclose(Y, xd @ wd.T, rtol=0, atol=1e-12 * np.abs(xd).sum())
