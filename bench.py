@@ -218,6 +218,48 @@ class Step:
                 raise RuntimeError(f"{name}: status {st} ({self.bq.bq_status_str(st)})")
 
 
+MM_M, MM_N, MM_SLICES = 4096, 7168, 6      # staged projection: six 4096 x 7168 slices, N = 7168
+MFMA_FP8_PEAK_TFLOPS = 5000.0               # MI355X dense fp8 matrix-core peak
+
+
+def gemm_bench(torch, bq, reps: int) -> dict:
+    """The dense MXFP8 GEMM from a staged buffer (not part of the step): six bf16 slices
+    of 4096 x 7168 quantized into a 4096 x 43008 staging buffer, times 7168 x 43008 MXFP8
+    weights, into bf16.  Synthetic N(0, 1) inputs drawn on the GPU with a fixed seed."""
+    K = MM_SLICES * COLS
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    xv = torch.empty((MM_M, K), dtype=torch.uint8, device="cuda")
+    xe = torch.empty((MM_M, K // 32), dtype=torch.uint8, device="cuda")
+    for j in range(MM_SLICES):
+        xs = torch.randn((MM_M, COLS), generator=g, device="cuda").to(torch.bfloat16)
+        bq.bq_quant_mx_slice(xs, j * COLS, xv, xe)
+    w = torch.randn((MM_N, K), generator=g, device="cuda").to(torch.bfloat16)
+    wv = torch.empty((MM_N, K), dtype=torch.uint8, device="cuda")
+    we = torch.empty((MM_N, K // 32), dtype=torch.uint8, device="cuda")
+    bq.bq_quant_mx(w, wv, we)
+    del w
+    y = torch.empty((MM_M, MM_N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        bq.bq_mm_mx(xv, xe, wv, we, y)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        bq.bq_mm_mx(xv, xe, wv, we, y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = 2.0 * MM_M * MM_N * K
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"workload": f"staged MXFP8 GEMM {MM_M}x{MM_N}x{K} (six 4096x7168 slices), bf16 out",
+            "bound": "mfma", "us_per_launch": round(us, 1), "achieved": round(tflops, 1),
+            "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops}
+
+
 def cpu_baseline(rows_per_rank: int) -> dict:
     """The oracle, single-threaded, on the first `rows_per_rank` rows of every rank."""
     import oracle
@@ -406,6 +448,7 @@ def main() -> int:
                          for k, v in per_next.items()},
     }
     line["accuracy"] = accuracy
+    line["gemm"] = gemm_bench(torch, bq, reps=10)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_rows)
         cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9

@@ -24,7 +24,7 @@ __all__ = [
     "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
     "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
     "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
-    "bq_quant_mx_f16", "bq_quant_mx_slice_f16",
+    "bq_quant_mx_f16", "bq_quant_mx_slice_f16", "bq_mm_mx",
     "bq_quant_mx_batch", "bq_dequant_mx_batch", "bq_ring_hop_mx", "bq_ring_hop_mx_batch",
     "bq_dequant_accum_mx", "bq_a2a_reduce_mx", "bq_allgather_dequant_mx",
     "bq_ring_allreduce_mx", "bq_a2a_allreduce_mx",
@@ -66,6 +66,7 @@ _SIGS = {
     "bq_quant_mx_slice": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
     "bq_mx_staging_bytes": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "bq_quant_mx_f16": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
+    "bq_mm_mx": [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I64, _P],
     "bq_quant_mx_slice_f16": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
     "bq_quant_mx_batch": [_I, _PP, _I64, _PP, _PP, _P],
     "bq_dequant_mx_batch": [_I, _PP, _PP, _I64, _PP, _P],
@@ -301,6 +302,18 @@ def bq_quant_mx_slice_f16(x, col_off: int, v, e8m0, capacity_rows: int | None = 
     _check("bq_quant_mx_slice_f16",
            _L().bq_quant_mx_slice_f16(_ptr(x), rows, cols, ldx, col_off, _ptr(v), ldv, _ptr(e8m0),
                                      lds, capacity_rows, _stream(stream)))
+
+
+def bq_mm_mx(xv, xe, wv, we, y, M: int | None = None, N: int | None = None,
+             K: int | None = None, stream=None) -> None:
+    """Y = bf16(X W^T) from MXFP8 X (xv (M, K) u8, xe (M, K/32) u8) and W (wv (N, K),
+    we (N, K/32)) into y (M, N) bf16; leading dimensions from the tensors' row strides."""
+    M = y.shape[0] if M is None else M
+    N = y.shape[1] if N is None else N
+    K = xv.shape[1] if K is None else K
+    _check("bq_mm_mx", _L().bq_mm_mx(_ptr(xv), xv.stride(0), _ptr(xe), xe.stride(0), _ptr(wv),
+                                    wv.stride(0), _ptr(we), we.stride(0), M, N, K, _ptr(y),
+                                    y.stride(0), _stream(stream)))
 
 
 def bq_mx_staging_bytes(capacity_rows: int, total_cols: int) -> tuple[int, int]:

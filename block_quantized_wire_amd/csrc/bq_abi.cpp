@@ -671,6 +671,31 @@ bq_status bq_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int6
         bq::launch_dequant_mx(v, ldv, e8m0, lds, rows, cols, y, ldy, as_stream(stream)));
 }
 
+bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t ldxe,
+                   const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe, int64_t M,
+                   int64_t N, int64_t K, uint16_t* y, int64_t ldy, void* stream) {
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if (M < 0 || N < 0 || K <= 0 || K % kBlk != 0 || M > lim || N > lim || K > lim)
+        return BQ_ERR_SIZE;
+    if (M == 0 || N == 0)
+        return BQ_OK;
+    if (!xv || !xe || !wv || !we || !y)
+        return BQ_ERR_NULL;
+    if (ldxv < K || ldwv < K || ldxe < K / BQ_MX_GROUP || ldwe < K / BQ_MX_GROUP || ldy < N)
+        return BQ_ERR_BOUNDS;
+    if (!aligned(xv, 16) || !aligned(wv, 16) || ldxv % 16 != 0 || ldwv % 16 != 0 ||
+        !aligned(xe, 4) || !aligned(we, 4) || ldxe % 4 != 0 || ldwe % 4 != 0 || !aligned(y, 2))
+        return BQ_ERR_ALIGN;
+    const Span ys = span(y, extent(M, N, ldy, 2));
+    if (overlaps(ys, span(xv, extent(M, K, ldxv, 1))) ||
+        overlaps(ys, span(xe, extent(M, K / BQ_MX_GROUP, ldxe, 1))) ||
+        overlaps(ys, span(wv, extent(N, K, ldwv, 1))) ||
+        overlaps(ys, span(we, extent(N, K / BQ_MX_GROUP, ldwe, 1))))
+        return BQ_ERR_ALIAS;
+    return launched(bq::launch_mm_mx(xv, ldxv, xe, ldxe, wv, ldwv, we, ldwe, M, N, K, y, ldy,
+                                     as_stream(stream)));
+}
+
 // ---- E4M3 128-block codec ------------------------------------------------------------------
 
 bq_status bq_quant_e4m3_b128(const uint16_t* x, int64_t n, uint8_t* v, float* scale,

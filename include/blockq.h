@@ -273,6 +273,24 @@ bq_status bq_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* parti
                               uint8_t* v_bcast, uint8_t* e_bcast, uint16_t* const* out,
                               void* stream);
 
+/* ==== The dense MXFP8 GEMM from staged inputs (P4 Behavior: mm_quantized_into) ========
+ *
+ * Y[m][n] = bf16_rne( sum over k of X[m][k] * W[n][k] ) for 0 <= m < M, 0 <= n < N:
+ * X is MXFP8 activations (an assembled staging buffer: xv u8[M][ldxv] E4M3 values and
+ * xe u8[M][ldxe] E8M0 bytes, byte g of a row scaling its columns [32g, 32g+32)), W is MXFP8
+ * weights in the same layout (wv u8[N][ldwv], we u8[N][ldwe]), both contiguous along K.
+ * Each product of two E4M3 values and their two scales is exact; the sums are binary32
+ * (matrix-core accumulation, K in steps of 128) and are rounded to bf16 once into y
+ * (bf16[M][ldy], caller-owned).  The summation order is fixed, so results are
+ * deterministic: the same inputs give the same bits, whether the staging buffer was
+ * filled by slices or by one call (P4 Validation).
+ * K must be a positive multiple of 128; M == 0 or N == 0 launches nothing.  ldxv, ldwv
+ * >= K and divisible by 16 with xv, wv 16-byte aligned; ldxe, ldwe >= K/32, divisible by
+ * 4, with xe, we 4-byte aligned; ldy >= N; y must not overlap an input. */
+bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t ldxe,
+                   const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe, int64_t M,
+                   int64_t N, int64_t K, uint16_t* y, int64_t ldy, void* stream);
+
 /* ==== E4M3 128-block codec: the format the INT8 codec replaces (P1 Summary, Why) ==== */
 
 /* Same block and footprint as the INT8 codec (132 bytes per 128 values): scale =

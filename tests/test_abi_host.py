@@ -279,3 +279,24 @@ def test_mx_f16_errors():
     assert f(x, rows, cols, 512, 64, v, 2048, e, 64, rows, S) == SIZE          # offset % 128
     assert f(x, rows, cols, 512, 1664, v, 2048, e, 64, rows, S) == BOUNDS      # past ldv
     assert f(x, rows, cols, 512, 0, v, 2048, e, 64, rows - 1, S) == BOUNDS     # capacity
+
+
+def test_mm_mx_errors():
+    M, N, K = 64, 48, 256
+    xv, xe, wv, we, y = A, A + 2 ** 20, A + 2 ** 21, A + 2 ** 22, A + 2 ** 23
+    f = L.bq_mm_mx
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, 0, y, N, S) == SIZE             # K == 0
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, 100, y, N, S) == SIZE           # K % 128
+    assert f(xv, K, xe, 8, wv, K, we, 8, -1, N, K, y, N, S) == SIZE
+    assert f(xv, K, xe, 8, wv, K, we, 8, 0, N, K, y, N, S) == OK               # nothing to do
+    assert f(None, K, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == NULL
+    assert f(xv, 128, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS         # ldxv < K
+    assert f(xv, K, xe, 4, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS           # ldxe < K/32
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, y, N - 1, S) == BOUNDS       # ldy < N
+    assert f(xv + 8, K, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
+    assert f(xv, K + 8, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
+    assert f(xv, K, xe + 1, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
+    assert f(xv, K, xe, 8, wv, K, we, 10, M, N, K, y, N, S) == ALIGN
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, y + 1, N, S) == ALIGN
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, xv + 256, N, S) == ALIAS
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, we + 16, N, S) == ALIAS
