@@ -14,10 +14,22 @@
 // 128 (byte 0 with opsel 0).  The 4 results of lane l are rows 4(l/16) + r, column l%16.
 // (Measured on MI355X with exact small-integer operands before this kernel was written.)
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; its 4 waves own 64 x 64
-// quadrants, each 4 x 4 MFMA blocks.  Per K step of 128 the workgroup stages the X and W
-// tiles (16 KB each) and their 128 x 4 scale bytes in LDS, double-buffered, so the
-// global loads of step k+1 are in flight while step k computes; one barrier per step.
+// Tiling: a 512-thread workgroup computes a 256 x 256 tile of Y; its 8 waves (two per
+// SIMD, so one can issue matrix instructions while the other waits on LDS) own 128 x 64
+// pieces, each 8 x 4 MFMA blocks: a wave reads 12 operand fragments from LDS per 32
+// MFMAs.
+// Per K step of 128 the workgroup stages the X and W tiles (32 KB each) and their
+// 256 x 4 scale bytes in LDS, double-buffered (132 KB), with gfx950's global-to-LDS
+// loads (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane i at
+// byte 16i), so no registers hold the staged data and the loads of step k+1 are in
+// flight while step k computes; one barrier per step.  A tile row is 128 contiguous
+// bytes; its 16-byte chunk c sits in slot c ^ ((row >> 1) & 7), so the 16 rows a
+// fragment read touches at one chunk fall in 16 distinct 16-byte bank groups.
+//
+// Tiles are handed out column-major, each XCD (every 8th workgroup) taking a contiguous
+// run: an XCD works through a band of W columns, whose tiles all its workgroups re-read
+// from its own L2, while the X rows (the smaller operand) are shared by all XCDs through
+// the last-level cache.
 #include "bq_device.h"
 #include "bq_launch.h"
 
@@ -28,8 +40,13 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTM = 128, kTN = 128, kTK = 128;   // workgroup tile
-constexpr int kRowPad = kTK + 16;                 // LDS row stride of a staged tile (bytes)
+constexpr int kTM = 256, kTN = 256, kTK = 128;   // workgroup tile
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kWM = 128, kWN = 64;                // wave tile
+constexpr int kWavesN = kTN / kWN;                // wave grid: (kTM / kWM) x kWavesN
+constexpr int kFA = kWM / 16, kFB = kWN / 16;     // MFMA blocks per wave tile side
+constexpr int kWaveLoads = kTM * kTK / 1024 / kWaves;   // 1 KB loads per wave per operand
+constexpr int kScaleRows = kTM / kWaves;                 // scale rows per wave per operand
 
 struct MmArgs {
     const uint8_t* xv;
@@ -39,122 +56,125 @@ struct MmArgs {
     uint16_t* y;
     int64_t ldxv, ldxe, ldwv, ldwe, ldy;
     int32_t M, N, K;
-    int32_t tiles_n;   // column tiles
+    int32_t tiles_m, tiles_n;   // row and column tiles
 };
 
 struct Stage {
-    uint8_t a[kTM * kRowPad];
-    uint8_t b[kTN * kRowPad];
-    uint32_t as[kTM];   // 4 E8M0 bytes (the 4 K-blocks of the step) per row
-    uint32_t bs[kTN];
+    uint8_t a[kTM * kTK];   // rows of 128 bytes, chunks swizzled (see chunk_slot)
+    uint8_t b[kTN * kTK];
+    // the 4 E8M0 bytes (the step's 4 K blocks) of each row: word 64w + j holds X row
+    // kScaleRows*w + j for j < 32 and W row kScaleRows*w + j - 32 for j >= 32
+    uint32_t sc[kTM + kTN];
 };
 
-// The global loads of one K step: 4 16-byte chunks of the X tile and 4 of the W tile per
-// thread (8 chunks per 128-byte row), and one scale word (threads 0-127: X rows,
-// 128-255: W rows).  Rows beyond M (N) are clamped to the last row; their results are
-// never stored.
-struct Prefetch {
-    u32x4 a[4], b[4];
-    uint32_t s;
-};
+__device__ __forceinline__ uint32_t x_scale_word(const Stage& st, int row) {
+    return st.sc[(row / kScaleRows) * 64 + row % kScaleRows];
+}
+__device__ __forceinline__ uint32_t w_scale_word(const Stage& st, int row) {
+    return st.sc[(row / kScaleRows) * 64 + 32 + row % kScaleRows];
+}
 
-__device__ __forceinline__ void load_step(const MmArgs& p, int m0, int n0, int k0, int tid,
-                                          Prefetch& f) {
+__device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// Issue the global-to-LDS loads of one K step into `st`: wave w fills 1 KB pieces
+// w*kWaveLoads .. of each operand (64 lanes x 16 bytes; lane i lands at byte 16i of the
+// piece and fetches the chunk that belongs in that slot), and the scale words of X and W
+// rows [32w, 32w+32) (4 bytes per lane: lanes 0-31 X, 32-63 W).  Rows beyond M (N) are clamped to the last row; their
+// results are never stored.
+__device__ __forceinline__ void load_step(const MmArgs& p, Stage& st, int m0, int n0, int k0,
+                                          int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c >> 3, col = (c & 7) * 16;
+    for (int j = 0; j < kWaveLoads; ++j) {
+        const int piece = wave * kWaveLoads + j;
+        const int u = piece * 64 + lane;              // 16-byte unit of the tile
+        const int row = u >> 3;
+        const int c = chunk_slot(row, u & 7);         // the slot's chunk (the map is an involution)
         const int ma = min(m0 + row, p.M - 1), nb = min(n0 + row, p.N - 1);
-        f.a[i] = ld16(p.xv + (int64_t)ma * p.ldxv + k0 + col);
-        f.b[i] = ld16(p.wv + (int64_t)nb * p.ldwv + k0 + col);
+        __builtin_amdgcn_global_load_lds(p.xv + (int64_t)ma * p.ldxv + k0 + 16 * c,
+                                         st.a + piece * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.wv + (int64_t)nb * p.ldwv + k0 + 16 * c,
+                                         st.b + piece * 1024, 16, 0, 0);
     }
-    if (tid < kTM) {
-        const int ma = min(m0 + tid, p.M - 1);
-        f.s = *reinterpret_cast<const uint32_t*>(p.xe + (int64_t)ma * p.ldxe + k0 / 32);
-    } else {
-        const int nb = min(n0 + tid - kTM, p.N - 1);
-        f.s = *reinterpret_cast<const uint32_t*>(p.we + (int64_t)nb * p.ldwe + k0 / 32);
-    }
+    const int r = kScaleRows * wave + (lane & 31);
+    const uint8_t* src = lane < 32
+        ? p.xe + (int64_t)min(m0 + r, p.M - 1) * p.ldxe + k0 / 32
+        : p.we + (int64_t)min(n0 + r, p.N - 1) * p.ldwe + k0 / 32;
+    __builtin_amdgcn_global_load_lds(src, st.sc + 64 * wave, 4, 0, 0);
 }
 
-__device__ __forceinline__ void store_step(Stage& st, int tid, const Prefetch& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4*>(st.a + row * kRowPad + col) = f.a[i];
-        *reinterpret_cast<u32x4*>(st.b + row * kRowPad + col) = f.b[i];
-    }
-    if (tid < kTM)
-        st.as[tid] = f.s;
-    else
-        st.bs[tid - kTM] = f.s;
-}
+// Wait for this wave's global-to-LDS loads (the barrier that follows publishes them).
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One 16 x 128 operand fragment of a lane from a staged tile: row `r`, K bytes
-// [16g, 16g+16) and [64+16g, 64+16g+16).
+// [16g, 16g+16) and [64+16g, 64+16g+16) (chunks g and 4+g).
 __device__ __forceinline__ i32x8 frag(const uint8_t* tile, int r, int g) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + r * kRowPad + 16 * g);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + r * kRowPad + 64 + 16 * g);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + r * kTK + 16 * chunk_slot(r, g));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + r * kTK + 16 * chunk_slot(r, 4 + g));
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-__global__ __launch_bounds__(256) void k_mm_mx(MmArgs p) {
+// Tile index (column-major tile order) of workgroup `bid`: with T tiles and T divisible
+// by 8, XCD x (= bid % 8) takes the contiguous run [x T/8, (x+1) T/8).
+__device__ __forceinline__ int tile_of(int bid, int tiles) {
+    if (tiles % 8 != 0)
+        return bid;
+    return (bid % 8) * (tiles / 8) + bid / 8;
+}
+
+__global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
     __shared__ Stage stage[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    const int tile = blockIdx.x;
-    const int m0 = (tile / p.tiles_n) * kTM, n0 = (tile % p.tiles_n) * kTN;
+    const int wm = (wave / kWavesN) * kWM, wn = (wave % kWavesN) * kWN;
+    const int tile = tile_of(blockIdx.x, p.tiles_m * p.tiles_n);
+    const int m0 = (tile % p.tiles_m) * kTM, n0 = (tile / p.tiles_m) * kTN;
     const int r16 = lane & 15, g = lane >> 4;
 
-    f32x4 acc[4][4];
+    f32x4 acc[kFA][kFB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kFA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < kFB; ++b)
             acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = p.K / kTK;
-    Prefetch f;
-    load_step(p, m0, n0, 0, tid, f);
-    store_step(stage[0], tid, f);
+    load_step(p, stage[0], m0, n0, 0, wave, lane);
+    wait_loads();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more)
-            load_step(p, m0, n0, (kt + 1) * kTK, tid, f);
+            load_step(p, stage[(kt + 1) & 1], m0, n0, (kt + 1) * kTK, wave, lane);
         const Stage& st = stage[kt & 1];
-        i32x8 bf[4];
-        int bsc[4];
+        i32x8 bf[kFB];
+        int bsc[kFB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < kFB; ++b) {
             const int n = wn + 16 * b + r16;
             bf[b] = frag(st.b, n, g);
-            bsc[b] = (int)((st.bs[n] >> (8 * g)) & 0xFFu);
+            bsc[b] = (int)((w_scale_word(st, n) >> (8 * g)) & 0xFFu);
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < kFA; ++a) {
             const int m = wm + 16 * a + r16;
             const i32x8 af = frag(st.a, m, g);
-            const int asc = (int)((st.as[m] >> (8 * g)) & 0xFFu);
+            const int asc = (int)((x_scale_word(st, m) >> (8 * g)) & 0xFFu);
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < kFB; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     af, bf[b], acc[a][b], 0, 0, 0, asc, 0, bsc[b]);
         }
-        if (more)
-            store_step(stage[(kt + 1) & 1], tid, f);
+        wait_loads();
         __syncthreads();
     }
 
     // epilogue: lane l holds rows 4(l/16) + r of column l%16 of each 16 x 16 block
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < kFA; ++a) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < kFB; ++b) {
             const int col = n0 + wn + 16 * b + r16;
             const uint32_t lo = pack_bf16x2(acc[a][b].x, acc[a][b].y);
             const uint32_t hi = pack_bf16x2(acc[a][b].z, acc[a][b].w);
@@ -191,8 +211,9 @@ hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int6
     a.N = (int32_t)N;
     a.K = (int32_t)K;
     const int64_t tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
+    a.tiles_m = (int32_t)tm;
     a.tiles_n = (int32_t)tn;
-    return launch1(k_mm_mx, dim3((unsigned)(tm * tn)), dim3(256), stream, a);
+    return launch1(k_mm_mx, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
 }
 
 }  // namespace bq
