@@ -27,8 +27,8 @@
 //    The fp64 product errs by less than 2^-51, so it rounds to the same binary32.
 //    Quotients below the normal range round to 0 (INT8) or to a zero E4M3 code of the
 //    right sign either way.  r is rcp(s) in fp64 refined by two Newton steps.
-//    On MI355X non-packed fp32 and fp64 instructions issue at the same rate, so this
-//    costs about what a reciprocal multiply plus a near-tie check did, with no branch.
+//    On MI355X non-packed fp32 and fp64 instructions issue at the same rate, so the
+//    fp64 product costs little more than an fp32 one, with no branch.
 //
 // Conversions use gfx950's packed instructions, whose rounding is the codecs':
 // v_cvt_pk_bf16_f32 rounds binary32 to bf16 to nearest even (subnormals kept, overflow
