@@ -341,7 +341,7 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not "
               "supported (a simulated rank is a separate HBM buffer on the one GPU)",
               file=sys.stderr)
         return 2
