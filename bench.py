@@ -260,6 +260,33 @@ def gemm_bench(torch, bq, reps: int) -> dict:
             "flops_per_launch": flops}
 
 
+def copy_reference(torch, stream, total_bytes: int, reps: int) -> dict:
+    """A plain device-to-device copy (torch's) moving total_bytes per launch, half read and half
+    written: the rate a kernel of that many algorithmic bytes could reach if it did nothing but
+    stream them.  Timed like the step's kernels: reps back-to-back launches on the same stream
+    between one pair of HIP events, the sources rotating over at least 1 GiB so they are cold in
+    the last-level cache."""
+    half = total_bytes // 2
+    nsrc = max(2, (1 << 30) // half + 1)
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsrc)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            dst[i % 2].copy_(src[i % nsrc])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            dst[i % 2].copy_(src[(i + 3) % nsrc])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    return {"bytes_per_launch": 2 * half, "us_per_launch": round(us, 2),
+            "gbs": round(2 * half / (us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(rows_per_rank: int) -> dict:
     """The oracle, single-threaded, on the first `rows_per_rank` rows of every rank."""
     import oracle
@@ -418,6 +445,7 @@ def main() -> int:
     per_next = time_kinds(step.next_kernels)
     dom_name = max(per, key=lambda k: per[k]["us_per_step"])
     dom = per[dom_name]
+    copy_ref = copy_reference(torch, step.stream, dom["bytes_per_launch"], max(reps, 20))
 
     # accuracy on input set 0, outside the timed regions: the all-reduce outputs against
     # the exact (fp64) sum of the bf16 partials, the codec round trips against their input
@@ -480,7 +508,10 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["frac"], 4),
                      "bytes_per_launch": dom["bytes_per_launch"],
                      "us_per_launch": round(dom["us_per_launch"], 2),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # a plain device copy of the same bytes per launch, timed the same way
+                     "copy_same_bytes": dict(copy_ref, kernel_over_copy=round(
+                         dom["gbs"] / copy_ref["gbs"], 3))},
         "kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
                         "launches_per_step": v["launches_per_step"],
                         "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
