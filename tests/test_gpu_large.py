@@ -48,9 +48,10 @@ def sampled_rows(rows: int, cols: int, seed: int) -> np.ndarray:
     return np.unique(np.concatenate([edge, rng.integers(1, rows - 1, 8)]))
 
 
-def fill(cfg: int, rank: int, rows: int, cols: int, period: int) -> torch.Tensor:
-    """rows x cols bf16 bits on the device, flat: row r is rank's generator row r % period."""
-    base = torch.from_numpy(workloads.rows(cfg, rank, 0, period, cols).view(np.int16)).to("cuda")
+def fill(cfg: int, rank: int, rows: int, cols: int, period: int, fmt: str = "bf16") -> torch.Tensor:
+    """rows x cols bf16 (or binary16) bits on the device, flat: row r is rank's generator row
+    r % period."""
+    base = torch.from_numpy(workloads.rows(cfg, rank, 0, period, cols, fmt=fmt).view(np.int16)).to("cuda")
     out = torch.empty(rows * cols, dtype=torch.int16, device="cuda")
     o = out.view(rows, cols)
     for r0 in range(0, rows, period):
@@ -60,8 +61,10 @@ def fill(cfg: int, rank: int, rows: int, cols: int, period: int) -> torch.Tensor
     return out
 
 
-def gen_rows(cfg: int, rank: int, rows: np.ndarray, cols: int, period: int) -> np.ndarray:
-    return np.concatenate([workloads.rows(cfg, rank, int(r) % period, 1, cols) for r in rows])
+def gen_rows(cfg: int, rank: int, rows: np.ndarray, cols: int, period: int,
+             fmt: str = "bf16") -> np.ndarray:
+    return np.concatenate([workloads.rows(cfg, rank, int(r) % period, 1, cols, fmt=fmt)
+                           for r in rows])
 
 
 def take(t: torch.Tensor, rows: np.ndarray, per_row: int, dtype) -> np.ndarray:
@@ -187,6 +190,28 @@ def test_mx_2d_past_2p31():
     assert_same(take(v, rows, MX_COLS, np.uint8), wv, "values")
     assert_same(take(e, rows, MX_COLS // 32, np.uint8), we, "scales")
     assert_same(take(y, rows, MX_COLS, np.uint16), oracle.dequant_mx(wv, we), "bf16")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_mx_staged_slices_past_2p31(fmt):
+    """Six 49,933 x 7168 slices (bf16, or binary16) quantized at offsets 0, 7168, ..., 35840
+    of a 49,933 x 43008 staging buffer, whose last rows start past byte 2^31; sampled rows
+    equal the oracle's quantization of the concatenated slices."""
+    J, K = 6, 7168
+    rows = sampled_rows(MX_ROWS, MX_COLS, 6)
+    say(f"large: mx staged {fmt} slices {J}x{MX_ROWS}x{K} -> {MX_ROWS}x{MX_COLS}")
+    v = empty((MX_ROWS, MX_COLS), np.uint8)
+    e = empty((MX_ROWS, MX_COLS // 32), np.uint8)
+    quant = bq.bq_quant_mx_slice if fmt == "bf16" else bq.bq_quant_mx_slice_f16
+    for j in range(J):
+        x = fill(4, j, MX_ROWS, K, MX_P, fmt).view(MX_ROWS, K)
+        quant(x, K * j, v, e)
+        sync()
+        del x
+    sub = np.concatenate([gen_rows(4, j, rows, K, MX_P, fmt) for j in range(J)], axis=1)
+    wv, we = oracle.quant_mx(sub) if fmt == "bf16" else oracle.quant_mx_f16(sub)
+    assert_same(take(v, rows, MX_COLS, np.uint8), wv, "values")
+    assert_same(take(e, rows, MX_COLS // 32, np.uint8), we, "scales")
 
 
 def test_mm_mx_weights_past_2p31_bytes():
