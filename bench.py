@@ -60,9 +60,13 @@ B_E4M3 = 256 + 132
 
 
 def kernel_source_digest() -> str:
+    """Digest of the device code (the .hip sources and the headers they include): the HBM
+    counters in profiles/ stay valid while it is unchanged; host-side validation may change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_wire_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -584,6 +584,19 @@ int64_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
     return rows == 0 ? 0 : ((rows - 1) * ld + cols) * elem;
 }
 
+// A 2-D operand may span at most 2^48 bytes, far beyond any device's memory, so that extent()
+// above and the kernels' 64-bit row * ld products cannot overflow.  Checked without overflow
+// for rows, cols >= 0 and cols <= ld.
+constexpr int64_t kMaxExtentBytes = (int64_t)1 << 48;
+bool extent_fits(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+    const int64_t lim = kMaxExtentBytes / elem;
+    if (rows == 0)
+        return true;
+    if (ld > lim)
+        return false;
+    return rows == 1 || ld <= (lim - cols) / (rows - 1);
+}
+
 }  // namespace
 
 namespace {
@@ -596,6 +609,9 @@ bq_status quant_mx_2d(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
     if (!x || !v || !e8m0)
         return BQ_ERR_NULL;
     if (ldx < cols || ldv < cols || lds < cols / BQ_MX_GROUP)
+        return BQ_ERR_BOUNDS;
+    if (!extent_fits(rows, cols, ldx, 2) || !extent_fits(rows, cols, ldv, 1) ||
+        !extent_fits(rows, cols / BQ_MX_GROUP, lds, 1))
         return BQ_ERR_BOUNDS;
     if (!aligned(x, 16) || !aligned(v, 16) || !aligned(e8m0, 4) || ldx % 8 != 0 ||
         ldv % 16 != 0 || lds % 4 != 0)
@@ -615,7 +631,7 @@ bq_status quant_mx_slice(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     BQ_TRY(check_mx_shape(rows, cols));
     if (col_off < 0 || col_off % kBlk != 0 || ldv < 0 || ldv % kBlk != 0)
         return BQ_ERR_SIZE;
-    if (col_off + cols > ldv || lds < ldv / BQ_MX_GROUP || rows > capacity_rows)
+    if (col_off > ldv || cols > ldv - col_off || lds < ldv / BQ_MX_GROUP || rows > capacity_rows)
         return BQ_ERR_BOUNDS;
     if (rows == 0 || cols == 0)
         return BQ_OK;
@@ -660,6 +676,9 @@ bq_status bq_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int6
         return BQ_ERR_NULL;
     if (ldy < cols || ldv < cols || lds < cols / BQ_MX_GROUP)
         return BQ_ERR_BOUNDS;
+    if (!extent_fits(rows, cols, ldy, 2) || !extent_fits(rows, cols, ldv, 1) ||
+        !extent_fits(rows, cols / BQ_MX_GROUP, lds, 1))
+        return BQ_ERR_BOUNDS;
     if (!aligned(y, 16) || !aligned(v, 16) || !aligned(e8m0, 4) || ldy % 8 != 0 ||
         ldv % 16 != 0 || lds % 4 != 0)
         return BQ_ERR_ALIGN;
@@ -682,6 +701,10 @@ bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t l
     if (!xv || !xe || !wv || !we || !y)
         return BQ_ERR_NULL;
     if (ldxv < K || ldwv < K || ldxe < K / BQ_MX_GROUP || ldwe < K / BQ_MX_GROUP || ldy < N)
+        return BQ_ERR_BOUNDS;
+    if (!extent_fits(M, K, ldxv, 1) || !extent_fits(M, K / BQ_MX_GROUP, ldxe, 1) ||
+        !extent_fits(N, K, ldwv, 1) || !extent_fits(N, K / BQ_MX_GROUP, ldwe, 1) ||
+        !extent_fits(M, N, ldy, 2))
         return BQ_ERR_BOUNDS;
     if (!aligned(xv, 16) || !aligned(wv, 16) || ldxv % 16 != 0 || ldwv % 16 != 0 ||
         !aligned(xe, 4) || !aligned(we, 4) || ldxe % 4 != 0 || ldwe % 4 != 0 || !aligned(y, 2))

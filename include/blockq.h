@@ -16,6 +16,10 @@
  *     and E8M0 bytes are uint8_t, per-block scales are float (IEEE binary32).
  *   - n counts values; it must be a multiple of 128 (a block, P1 Summary; the per-rank
  *     shard rule of P2 Configuration).  n == 0 is valid and launches nothing.
+ *     Limits: n / 128 < 2^36 (else BQ_ERR_SIZE); a row-major operand of rows x cols with
+ *     row stride ld spans at most 2^48 bytes, ((rows - 1) * ld + cols) * element size
+ *     (else BQ_ERR_BOUNDS); the MXFP8 calls take rows * cols / 128 < 2^31 blocks, and
+ *     the GEMM M, N, K < 2^31 (else BQ_ERR_SIZE).
  *   - Layout of an INT8 or E4M3 block payload is planar: n payload bytes, and nb = n/128
  *     scales in a separate array.  Together they are 132 bytes per 128 values (P1
  *     Summary); a caller may place the scale array right after the payload in one

@@ -199,6 +199,15 @@ def test_mx_errors():
     assert L.bq_quant_mx(x, 0, cols, 512, v, 512, e, 16, S) == OK
     assert L.bq_dequant_mx(v, 512, e, 16, rows, cols, v + 64, 512, S) == ALIAS
     assert L.bq_dequant_mx(v, 512, e, 16, rows, cols, x, 500, S) == BOUNDS
+    # a row stride whose operand would span more than 2^48 bytes (and whose extent would
+    # overflow int64) is refused before any arithmetic on it
+    huge = 2 ** 62
+    assert L.bq_quant_mx(x, rows, cols, huge, v, 512, e, 16, S) == BOUNDS
+    assert L.bq_quant_mx(x, rows, cols, 512, v, huge, e, 16, S) == BOUNDS
+    assert L.bq_quant_mx(x, rows, cols, 512, v, 512, e, huge, S) == BOUNDS
+    assert L.bq_quant_mx(x, 2, cols, 2 ** 47, v, 512, e, 16, S) == BOUNDS      # 2^48 + 1024 bytes
+    assert L.bq_dequant_mx(v, huge, e, 16, rows, cols, x, 512, S) == BOUNDS
+    assert L.bq_dequant_mx(v, 512, e, 16, rows, cols, x, huge, S) == BOUNDS
 
 
 def test_mx_slice_errors():
@@ -211,6 +220,8 @@ def test_mx_slice_errors():
     assert f(x, rows, cols, cols, 0, v, total, e, total // 32 - 4, rows, S) == BOUNDS
     assert f(x, rows, cols, cols, 0, v, total, e, total // 32, rows - 1, S) == BOUNDS  # capacity
     assert f(x, rows, cols, cols, 0, None, total, e, total // 32, rows, S) == NULL
+    top = 2 ** 63 - 128                      # col_off + cols would overflow int64
+    assert f(x, rows, cols, cols, top, v, total, e, total // 32, rows, S) == BOUNDS
 
 
 def test_mx_collective_errors():
@@ -293,6 +304,12 @@ def test_mm_mx_errors():
     assert f(xv, 128, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS         # ldxv < K
     assert f(xv, K, xe, 4, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS           # ldxe < K/32
     assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, y, N - 1, S) == BOUNDS       # ldy < N
+    huge = 2 ** 62                                                             # extent > 2^48 bytes
+    assert f(xv, huge, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS
+    assert f(xv, K, xe, huge, wv, K, we, 8, M, N, K, y, N, S) == BOUNDS
+    assert f(xv, K, xe, 8, wv, huge, we, 8, M, N, K, y, N, S) == BOUNDS
+    assert f(xv, K, xe, 8, wv, K, we, huge, M, N, K, y, N, S) == BOUNDS
+    assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, y, huge, S) == BOUNDS
     assert f(xv + 8, K, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
     assert f(xv, K + 8, xe, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
     assert f(xv, K, xe + 1, 8, wv, K, we, 8, M, N, K, y, N, S) == ALIGN
