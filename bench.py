@@ -300,7 +300,6 @@ def cpu_baseline(rows_per_rank: int) -> dict:
     t0 = time.perf_counter()
     oracle.ring_allreduce_i8([p.reshape(-1) for p in parts])
     oracle.a2a_allreduce_i8([p.reshape(-1) for p in parts])
-    cat = np.concatenate(parts, axis=1)
     v = np.empty((R, W * COLS), np.uint8)
     e = np.empty((R, W * COLS // 32), np.uint8)
     for r in range(W):
@@ -309,7 +308,6 @@ def cpu_baseline(rows_per_rank: int) -> dict:
     ev, es = oracle.quant_e4m3_b128(parts[0])
     oracle.dequant_e4m3_b128(ev, es)
     dt = time.perf_counter() - t0
-    del cat
     frac = R / ROWS
     return {"seconds": dt, "frac": frac}
 

@@ -34,3 +34,12 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_runs_the_oracle_on_a_small_sample():
+    """bench.py's one-core CPU leg on 8 rows of every rank: the oracle's whole step runs and
+    the figure it reports is a positive rate for that fraction of the step."""
+    sys.path.insert(0, ROOT)
+    import bench
+    r = bench.cpu_baseline(8)
+    assert r["seconds"] > 0 and r["frac"] == 8 / bench.ROWS
