@@ -1,0 +1,183 @@
+"""Randomized GPU parity sweep: many small seeded cases of random shape against the oracle.
+
+Each case draws its sizes (ragged block counts, rows, padded strides, ranks, sources,
+owners) and a wide value mix: per-block magnitudes from 2^-130 to 2^90, values spread
+20 octaves below their block's top, random signs, 3% zeros, bf16 subnormals and 2%
+all-zero blocks.  Every output is compared bit for bit with the oracle, whose inputs are
+the same host arrays (payloads for a hop or an accumulate are the oracle's own
+quantization of drawn tensors, never the GPU's).  The case about to run is printed
+first, so a failure names its seed and shape.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import empty, host, say, sync, to_dev
+
+from block_quantized_wire_amd import build as _build
+
+if _build.stale():
+    _build.build()
+import block_quantized_wire_amd as bq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+def assert_same(got, want, what):
+    got, want = np.asarray(got).reshape(-1), np.asarray(want).reshape(-1)
+    assert got.shape == want.shape, what
+    if got.dtype == np.float32:
+        got, want = got.view(np.uint32), want.view(np.uint32)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}: " \
+                          f"got {got[bad[:5]]} want {want[bad[:5]]}"
+
+
+def draw(rng, n: int, lo: int = -130, hi: int = 90, fmt: str = "bf16") -> np.ndarray:
+    """n finite values (n a multiple of 32) as bf16 (or binary16) bit patterns, truncated
+    toward zero from binary32; the magnitudes are chosen per 32-value group."""
+    groups = n // 32
+    top = rng.integers(lo, hi + 1, groups).repeat(32)
+    e = top - rng.integers(0, 21, n)
+    m = 1.0 + rng.random(n)
+    v = np.ldexp(m, e) * np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    v[rng.random(n) < 0.03] = 0.0
+    v.reshape(groups, 32)[rng.random(groups) < 0.02] = 0.0
+    if fmt == "f16":
+        v = np.clip(v, -65504.0, 65504.0)
+        return v.astype(np.float32).astype(np.float16).view(np.uint16)   # round, then finite
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def blocks(rng, lo=1, hi=300) -> int:
+    return 128 * int(rng.integers(lo, hi + 1))
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_i8_codec_hop_and_accumulate(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = blocks(rng)
+    nsrc = int(rng.integers(1, 65))
+    in_place = bool(rng.integers(0, 2))
+    say(f"random i8 seed={seed} n={n} nsrc={nsrc} hop in place={in_place}")
+    x = draw(rng, n)
+    q, s = empty(n, np.int8), empty(n // 128, np.float32)
+    bq.bq_quant_i8(to_dev(x), q, s, n=n)
+    y = empty(n, np.uint16)
+    bq.bq_dequant_i8(q, s, y, n=n)
+    sync()
+    wq, ws = oracle.quant_i8(x)
+    assert_same(host(q, np.int8), wq, "payload")
+    assert_same(host(s, np.float32), ws, "scales")
+    assert_same(host(y, np.uint16), oracle.dequant_i8(wq, ws), "materialized")
+    # hop: the oracle's payload of x plus a drawn local partial
+    local = draw(rng, n, lo=-130, hi=89)
+    qi, si = to_dev(wq), to_dev(ws)
+    if in_place:
+        qo, so = qi, si
+    else:
+        qo, so = empty(n, np.int8), empty(n // 128, np.float32)
+    bq.bq_ring_hop_i8(qi, si, to_dev(local), qo, so, n=n)
+    sync()
+    hq, hs = oracle.ring_hop_i8(wq, ws, local)
+    assert_same(host(qo, np.int8), hq, "hop payload")
+    assert_same(host(so, np.float32), hs, "hop scales")
+    # accumulate of nsrc payloads in source order
+    srcs = [oracle.quant_i8(draw(rng, n, hi=80)) for _ in range(nsrc)]
+    ya = empty(n, np.uint16)
+    bq.bq_dequant_accum_i8([to_dev(a) for a, _ in srcs], [to_dev(b) for _, b in srcs], ya, n=n)
+    sync()
+    want = oracle.dequant_accum_i8([a for a, _ in srcs], [b for _, b in srcs])
+    assert_same(host(ya, np.uint16), want, "accumulated bf16")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_i8_collectives(seed):
+    rng = np.random.default_rng(2000 + seed)
+    W = int(rng.integers(1, 9))
+    nseg = int(rng.integers(1, 9))
+    nsrc = int(rng.integers(1, 17))
+    n = W * blocks(rng, 1, 40)
+    m = nseg * blocks(rng, 1, 40)
+    say(f"random i8 collectives seed={seed} ring W={W} n={n}; owner step nseg={nseg} "
+        f"nsrc={nsrc} n={m}")
+    parts = [draw(rng, n, hi=80) for _ in range(W)]
+    wq, ws, wouts = oracle.ring_allreduce_i8(parts)
+    qw, sw = empty(n, np.int8), empty(n // 128, np.float32)
+    outs = [empty(n, np.uint16) for _ in range(W)]
+    bq.bq_ring_allreduce_i8([to_dev(p) for p in parts], qw, sw, outs, n=n)
+    sync()
+    assert_same(host(qw, np.int8), wq, "ring payloads")
+    assert_same(host(sw, np.float32), ws, "ring scales")
+    for r in range(W):
+        assert_same(host(outs[r], np.uint16), wouts[r], f"ring rank {r}")
+    srcs = [oracle.quant_i8(draw(rng, m, hi=80)) for _ in range(nsrc)]
+    qs, ss = [a for a, _ in srcs], [b for _, b in srcs]
+    oq, os_, oys, ored = oracle.a2a_reduce_i8(qs, ss, nseg)
+    qo, so, red = empty(m, np.int8), empty(m // 128, np.float32), empty(m, np.uint16)
+    ys = [empty(m // nseg, np.uint16) for _ in range(nseg)]
+    bq.bq_a2a_reduce_i8(nseg, [to_dev(a) for a in qs], [to_dev(b) for b in ss], qo, so, ys, red)
+    sync()
+    assert_same(host(qo, np.int8), oq, "owner payload")
+    assert_same(host(so, np.float32), os_, "owner scales")
+    assert_same(host(red, np.uint16), ored, "owner bf16 sums")
+    for j in range(nseg):
+        assert_same(host(ys[j], np.uint16), oys[j], f"owner {j} materialization")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_mx_and_e4m3(seed):
+    rng = np.random.default_rng(3000 + seed)
+    rows = int(rng.integers(1, 41))
+    cols = blocks(rng, 1, 20)
+    padv, pads = 16 * int(rng.integers(0, 3)), 4 * int(rng.integers(0, 3))
+    fmt = "f16" if rng.integers(0, 2) else "bf16"
+    n = blocks(rng)
+    nsrc = int(rng.integers(1, 65))
+    say(f"random mx seed={seed} {fmt} {rows}x{cols} pads=({padv},{pads}); flat n={n} "
+        f"nsrc={nsrc}; e4m3-b128")
+    # 2-D MXFP8 with padded strides (binary16 input: magnitudes within its range)
+    x = draw(rng, rows * cols, lo=-20, hi=14, fmt=fmt) if fmt == "f16" else draw(rng, rows * cols)
+    x = x.reshape(rows, cols)
+    ldv, lds = cols + padv, cols // 32 + pads
+    v, e = empty((rows, ldv), np.uint8), empty((rows, lds), np.uint8)
+    quant = bq.bq_quant_mx_f16 if fmt == "f16" else bq.bq_quant_mx
+    quant(to_dev(x), v, e, rows=rows, cols=cols, ldv=ldv, lds=lds)
+    y = empty((rows, cols), np.uint16)
+    bq.bq_dequant_mx(v, e, y, rows=rows, cols=cols, ldv=ldv, lds=lds)
+    sync()
+    wv, we = oracle.quant_mx_f16(x) if fmt == "f16" else oracle.quant_mx(x)
+    assert_same(host(v, np.uint8)[:, :cols], wv, "E4M3 values")
+    assert_same(host(e, np.uint8)[:, :cols // 32], we, "E8M0 scales")
+    assert_same(host(y, np.uint16), oracle.dequant_mx(wv, we), "MX bf16")
+    # flat MXFP8: hop in place, accumulate
+    xf = draw(rng, n, hi=80)
+    fv, fe = oracle.quant_mx_flat(xf)
+    local = draw(rng, n, hi=80)
+    vi, ei = to_dev(fv), to_dev(fe)
+    bq.bq_ring_hop_mx(vi, ei, to_dev(local), vi, ei, n=n)
+    sync()
+    hv, he = oracle.ring_hop_mx(fv, fe, local)
+    assert_same(host(vi, np.uint8), hv, "MX hop values")
+    assert_same(host(ei, np.uint8), he, "MX hop scales")
+    srcs = [oracle.quant_mx_flat(draw(rng, n, hi=80)) for _ in range(nsrc)]
+    ya = empty(n, np.uint16)
+    bq.bq_dequant_accum_mx([to_dev(a) for a, _ in srcs], [to_dev(b) for _, b in srcs], ya, n=n)
+    sync()
+    assert_same(host(ya, np.uint16), oracle.dequant_accum_mx([a for a, _ in srcs],
+                                                             [b for _, b in srcs]), "MX accumulate")
+    # E4M3 128-block codec
+    xe = draw(rng, n)
+    ev, es = empty(n, np.uint8), empty(n // 128, np.float32)
+    bq.bq_quant_e4m3_b128(to_dev(xe), ev, es, n=n)
+    ye = empty(n, np.uint16)
+    bq.bq_dequant_e4m3_b128(ev, es, ye, n=n)
+    sync()
+    wev, wes = oracle.quant_e4m3_b128(xe)
+    assert_same(host(ev, np.uint8), wev, "E4M3-b128 values")
+    assert_same(host(es, np.float32), wes, "E4M3-b128 scales")
+    assert_same(host(ye, np.uint16), oracle.dequant_e4m3_b128(wev, wes), "E4M3-b128 bf16")
