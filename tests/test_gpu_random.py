@@ -181,3 +181,39 @@ def test_random_mx_and_e4m3(seed):
     assert_same(host(ev, np.uint8), wev, "E4M3-b128 values")
     assert_same(host(es, np.float32), wes, "E4M3-b128 scales")
     assert_same(host(ye, np.uint16), oracle.dequant_e4m3_b128(wev, wes), "E4M3-b128 bf16")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_mm_mx(seed):
+    """Random GEMM shapes (ragged M and N, K up to 2048): operands are the oracle's MXFP8
+    quantization of drawn values, within the bound derived from the matrix cores'
+    arithmetic and deterministic; plus an exact small-integer case compared bit for bit."""
+    from test_gpu_mm_mx import block_max_sum, check_close
+    import torch
+    rng = np.random.default_rng(4000 + seed)
+    M, N = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    K = 128 * int(rng.integers(1, 17))
+    say(f"random mm_mx seed={seed} {M}x{N}x{K}")
+    xv, xe = oracle.quant_mx(draw(rng, M * K, lo=-30, hi=30).reshape(M, K))
+    wv, we = oracle.quant_mx(draw(rng, N * K, lo=-30, hi=30).reshape(N, K))
+    Y, S = oracle.mm_mx(xv, xe, wv, we)
+    B = block_max_sum(xv, xe, wv, we)
+    y = empty((M, N), np.uint16)
+    bq.bq_mm_mx(to_dev(xv), to_dev(xe), to_dev(wv), to_dev(we), y)
+    y2 = empty((M, N), np.uint16)
+    bq.bq_mm_mx(to_dev(xv), to_dev(xe), to_dev(wv), to_dev(we), y2)
+    sync()
+    got = host(y, np.uint16)
+    check_close(got, Y, S, B, K, "outputs")
+    assert np.array_equal(got, host(y2, np.uint16)), "not deterministic"
+    # exact: codes 0, +-1, +-2 and block scales in [2^-1, 2^1] keep every sum exact
+    codes = np.array([0x00, 0x38, 0x40, 0xB8, 0xC0], np.uint8)
+    xv = codes[rng.integers(0, 5, (M, K))]
+    wv = codes[rng.integers(0, 5, (N, K))]
+    xe = rng.integers(126, 129, (M, K // 32)).astype(np.uint8)
+    we = rng.integers(126, 129, (N, K // 32)).astype(np.uint8)
+    Y, _ = oracle.mm_mx(xv, xe, wv, we)
+    want = torch.from_numpy(Y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bq.bq_mm_mx(to_dev(xv), to_dev(xe), to_dev(wv), to_dev(we), y)
+    sync()
+    assert np.array_equal(host(y, np.uint16), want), "exact case differs"
