@@ -136,6 +136,15 @@ __device__ __forceinline__ uint32_t row_max16(uint32_t v) {
     return v;
 }
 
+// Max of a non-negative binary32 (as bits) over the 8 lanes of a half DPP row: one block
+// when a lane holds 16 values.
+__device__ __forceinline__ uint32_t half_row_max8(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max(v, dpp<0x141>(v));   // row_half_mirror
+    return v;
+}
+
 // Max over the 4 lanes of a quad (one MXFP8 group of 32 values).
 __device__ __forceinline__ uint32_t quad_max4(uint32_t v) {
     v = max(v, dpp<0xB1>(v));
@@ -337,12 +346,51 @@ struct Lanes {
 
 __device__ __forceinline__ int64_t tiles_of(int64_t nb) { return (nb + kTileBlocks - 1) / kTileBlocks; }
 
+// The same walk with 16 values per lane: a block is the 8 lanes of a half DPP row and a
+// wave64 tile is 8 blocks.  A lane then reads or writes its block's one-byte values as one
+// 16-byte vector, which the kernels whose one-byte side is an output (quantize, ring hop)
+// stream measurably faster; their bf16 side becomes two 16-byte vectors per lane.
+constexpr int kLaneVals16 = 16;
+constexpr int kTileBlocks16 = 8;
+struct Lanes16 {
+    uint32_t sub, off;
+    bool leader;     // first lane of the block: stores its scale
+    int64_t first;   // first tile of this wave
+    int64_t step;    // tiles between successive steps of this wave
+    __device__ explicit Lanes16(int U) {
+        const uint32_t lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        sub = lane >> 3;
+        off = (lane & 7) * kLaneVals16;
+        leader = (lane & 7) == 0;
+        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        step = (int64_t)gridDim.x * kWavesPerGroup * U;
+    }
+    // block of tile u of a step, counted from the step's first block
+    __device__ __forceinline__ uint32_t blk(int u) const { return (uint32_t)u * kTileBlocks16 + sub; }
+    // first value of this lane in tile u of a step, counted from the step's first value
+    __device__ __forceinline__ uint32_t val(int u) const { return blk(u) * kBlock + off; }
+};
+
+__device__ __forceinline__ int64_t tiles16_of(int64_t nb) {
+    return (nb + kTileBlocks16 - 1) / kTileBlocks16;
+}
+
 // Launch shape of the flat kernels: 256-thread workgroups of 4 waves, U tiles of 4
 // blocks per wave step; at most kMaxGroups workgroups in all (the `count` segments of a
 // batch, grid.y, share them).
 template <int U>
 dim3 grid_for(int64_t nb, int count) {
     const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks;
+    const int64_t want = (nb + per_group - 1) / per_group;
+    const int64_t cap = kMaxGroups / count > 0 ? kMaxGroups / count : 1;
+    return dim3((unsigned)(want < cap ? want : cap), (unsigned)count, 1);
+}
+
+// Launch shape of the kernels on the 16-values-per-lane walk (tiles of 8 blocks).
+template <int U>
+dim3 grid16_for(int64_t nb, int count) {
+    const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks16;
     const int64_t want = (nb + per_group - 1) / per_group;
     const int64_t cap = kMaxGroups / count > 0 ? kMaxGroups / count : 1;
     return dim3((unsigned)(want < cap ? want : cap), (unsigned)count, 1);

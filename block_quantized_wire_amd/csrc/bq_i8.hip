@@ -10,9 +10,12 @@
 //   ring hop      requantize fl32(fl32(q * scale) + local) block by block (one fused
 //                 reduce-scatter hop; the binary32 sums are requantized directly).
 //
-// All kernels are HBM streaming kernels: 16-byte bf16 and 8-byte INT8 vectors per lane,
-// per-block amax through DPP row reductions (no LDS), no atomics, and a fixed order of
-// every floating-point operation, so results are deterministic and bit-reproducible.
+// All kernels are HBM streaming kernels with 16-byte vectors, per-block amax through DPP
+// reductions (no LDS), no atomics, and a fixed order of every floating-point operation, so
+// results are deterministic and bit-reproducible.  The kernels that write the INT8 payload
+// (quantize, ring hop) give a lane 16 values -- one 16-byte payload vector, two of bf16 --
+// and the others give it 8 (one 16-byte bf16 vector, 8 payload bytes): each side's
+// stores then cover whole contiguous 1 KB runs per wave instruction.
 // Every kernel takes a batch of equal-size segments (grid.y = segment) so that one
 // launch covers all simulated ranks of a collective step.
 #include "bq_device.h"
@@ -58,32 +61,37 @@ struct AccumArgs {
     int64_t seg_n;            // values per segment
 };
 
+// A lane holds 16 values (Lanes16): its block's payload bytes are one 16-byte store.
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
     int8_t* __restrict__ q = a.q[blockIdx.y];
     float* __restrict__ s = a.s[blockIdx.y];
-    const Lanes L(U);
-    const int64_t nt = tiles_of(a.nb);
+    const Lanes16 L(U);
+    const int64_t nt = tiles16_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
-        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
-        u32x4 xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            xv[u] = (L.blk(u) < left) ? ld16(x + b0 * kBlock + L.val(u)) : u32x4{};
+        const int64_t b0 = t0 * kTileBlocks16, left = a.nb - b0;   // uniform
+        u32x4 xv[U][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float f[8];
-            unpack_bf16x8(xv[u], f);
+            const bool in = L.blk(u) < left;
+            xv[u][0] = in ? ld16(x + b0 * kBlock + L.val(u)) : u32x4{};
+            xv[u][1] = in ? ld16(x + b0 * kBlock + L.val(u) + 8) : u32x4{};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[16];
+            unpack_bf16x8(xv[u][0], f);
+            unpack_bf16x8(xv[u][1], f + 8);
             float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
                 m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float amax = __uint_as_float(half_row_max8(__float_as_uint(m)));
             const float sc = i8_scale(amax);
-            const u32x2 qv = quant_i8x8(f, sc);
+            const u32x2 lo = quant_i8x8(f, sc), hi = quant_i8x8(f + 8, sc);
             if (L.blk(u) < left) {
-                st8(q + b0 * kBlock + L.val(u), qv);
+                st16(q + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
                 if (L.leader)
                     s[b0 + L.blk(u)] = sc;
             }
@@ -131,36 +139,38 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_i8(HopArgs a) {
     const uint16_t* __restrict__ local = a.local[blockIdx.y];
     int8_t* q_out = a.q_out[blockIdx.y];
     float* s_out = a.s_out[blockIdx.y];
-    const Lanes L(U);
-    const int64_t nt = tiles_of(a.nb);
+    const Lanes16 L(U);
+    const int64_t nt = tiles16_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
-        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
-        u32x2 qv[U];
-        u32x4 lv[U];
+        const int64_t b0 = t0 * kTileBlocks16, left = a.nb - b0;   // uniform
+        u32x4 qv[U], lv[U][2];
         float sv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool in = L.blk(u) < left;
-            qv[u] = in ? ld8(q_in + b0 * kBlock + L.val(u)) : u32x2{};
+            qv[u] = in ? ld16(q_in + b0 * kBlock + L.val(u)) : u32x4{};
             sv[u] = in ? s_in[b0 + L.blk(u)] : 0.0f;
-            lv[u] = in ? ld16(local + b0 * kBlock + L.val(u)) : u32x4{};
+            lv[u][0] = in ? ld16(local + b0 * kBlock + L.val(u)) : u32x4{};
+            lv[u][1] = in ? ld16(local + b0 * kBlock + L.val(u) + 8) : u32x4{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float deq[8], loc[8], sum[8];
-            dequant_i8x8(qv[u], sv[u], deq);        // rounded products ...
-            unpack_bf16x8(lv[u], loc);
+            float deq[16], loc[16], sum[16];
+            dequant_i8x8(u32x2{qv[u].x, qv[u].y}, sv[u], deq);      // rounded products ...
+            dequant_i8x8(u32x2{qv[u].z, qv[u].w}, sv[u], deq + 8);
+            unpack_bf16x8(lv[u][0], loc);
+            unpack_bf16x8(lv[u][1], loc + 8);
             float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sum[i] = deq[i] + loc[i];            // ... then rounded adds
+            for (int i = 0; i < 16; ++i) {
+                sum[i] = deq[i] + loc[i];                            // ... then rounded adds
                 m = __builtin_fmaxf(m, __builtin_fabsf(sum[i]));
             }
-            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float amax = __uint_as_float(half_row_max8(__float_as_uint(m)));
             const float sc = i8_scale(amax);
-            const u32x2 out = quant_i8x8(sum, sc);
+            const u32x2 lo = quant_i8x8(sum, sc), hi = quant_i8x8(sum + 8, sc);
             if (L.blk(u) < left) {
-                st8(q_out + b0 * kBlock + L.val(u), out);
+                st16(q_out + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
                 if (L.leader)
                     s_out[b0 + L.blk(u)] = sc;
             }
@@ -255,9 +265,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_i8(AccumArgs a) {
     }
 }
 
-constexpr int kUQuant = 2;
+constexpr int kUQuant = 1;
 constexpr int kUDequant = 2;
-constexpr int kUHop = 2;
+constexpr int kUHop = 1;
 constexpr int kUAccum = 2;
 
 }  // namespace
@@ -271,7 +281,7 @@ hipError_t launch_quant(int count, const uint16_t* const* x, int8_t* const* q,
         a.s[i] = s[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_quant_i8<kUQuant>, grid_for<kUQuant>(a.nb, count), dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_i8<kUQuant>, grid16_for<kUQuant>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant(int count, const int8_t* const* q, const float* const* s,
@@ -303,7 +313,7 @@ hipError_t launch_ring_hop(int count, const int8_t* const* q_in, const float* co
         a.s_out[i] = s_out[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_ring_hop_i8<kUHop>, grid_for<kUHop>(a.nb, count), dim3(kGroupThreads), stream, a);
+    return launch1(k_ring_hop_i8<kUHop>, grid16_for<kUHop>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_accum(int nsrc, const int8_t* const* q, const float* const* s,
