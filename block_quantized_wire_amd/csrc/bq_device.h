@@ -145,6 +145,17 @@ __device__ __forceinline__ uint32_t half_row_max8(uint32_t v) {
     return v;
 }
 
+// Max over a pair of lanes (one MXFP8 group of 32 values when a lane holds 16).
+__device__ __forceinline__ uint32_t pair_max2(uint32_t v) {
+    return max(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+}
+
+// The 4 E8M0 bytes of a block whose lanes hold 16 values -- one byte per lane pair of its
+// half row -- packed into a word in the block's first lane, group 0 in byte 0.
+__device__ __forceinline__ uint32_t gather_e8m0_pairs(uint32_t byte) {
+    return byte | (dpp<0x102>(byte) << 8) | (dpp<0x104>(byte) << 16) | (dpp<0x106>(byte) << 24);
+}
+
 // Max over the 4 lanes of a quad (one MXFP8 group of 32 values).
 __device__ __forceinline__ uint32_t quad_max4(uint32_t v) {
     v = max(v, dpp<0xB1>(v));

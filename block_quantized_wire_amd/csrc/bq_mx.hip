@@ -12,8 +12,11 @@
 //   scale = fl32(amax/448), v = e4m3_rne_sat(fl32(x/scale)), all-zero block -> scale 0
 //   and bytes 0x00; dequantize y = bf16_rne(fl32(e4m3 * scale)).
 //
-// Same lane layout as the INT8 kernels: 8 values per lane, one 128-column block per DPP
-// row, so an MXFP8 group of 32 is one quad of lanes and its amax takes two DPP steps.
+// Same lane layouts as the INT8 kernels.  The quantizers give a lane 16 values (a
+// 128-column block per half DPP row; an MXFP8 group of 32 is a lane pair, its amax one DPP
+// step) so that each lane stores its codes as one 16-byte vector; the dequantizers give it
+// 8 (a block per DPP row, a group per quad) so that each lane stores one 16-byte bf16
+// vector.
 #include "bq_device.h"
 #include "bq_launch.h"
 
@@ -53,9 +56,10 @@ struct MxLane {
     bool in;
 };
 
-__device__ __forceinline__ MxLane mx_lane(const MxArgs& a, int64_t tile, int sub) {
+__device__ __forceinline__ MxLane mx_lane(const MxArgs& a, int64_t tile, int sub,
+                                          int tile_blocks = kTileBlocks) {
     MxLane m;
-    const int64_t b = tile * kTileBlocks + sub;
+    const int64_t b = tile * tile_blocks + sub;
     m.in = b < (int64_t)a.nblocks;
     const uint32_t bb = m.in ? (uint32_t)b : 0u;
     m.row = a.per_row.div(bb);
@@ -77,46 +81,65 @@ struct Walk {
     }
 };
 
+// The same walk with 16 values per lane: tiles of 8 blocks, a block per half DPP row.
+struct Walk16 {
+    int sub, off;
+    int64_t first, step;
+    __device__ explicit Walk16(int U) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // uniform
+        sub = lane >> 3;
+        off = (lane & 7) * kLaneVals16;
+        first = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * U;
+        step = (int64_t)gridDim.x * kWavesPerGroup * U;
+    }
+};
+
+// A lane holds 16 values (Walk16): a 32-column group is a lane pair, and the block's codes
+// are one 16-byte store per lane.
 // F16: the input is IEEE binary16 (b12x pull request #241, Behavior: BF16 or FP16 slices);
 // the group byte then comes from the binary32 amax rule, which is exact for any amax.
 template <int U, bool F16>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
-    const Walk w(U);
+    const Walk16 w(U);
     const int lane = threadIdx.x & 63;
-    const int64_t nt = ((int64_t)a.nblocks + kTileBlocks - 1) / kTileBlocks;
+    const int64_t nt = ((int64_t)a.nblocks + kTileBlocks16 - 1) / kTileBlocks16;
     for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
-        u32x4 xv[U];
+        u32x4 xv[U][2];
         MxLane ml[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            ml[u] = mx_lane(a, t0 + u, w.sub);
-            xv[u] = ml[u].in ? ld16(a.x + ml[u].row * a.ldx + ml[u].cb * kBlock + w.off) : u32x4{};
+            ml[u] = mx_lane(a, t0 + u, w.sub, kTileBlocks16);
+            const uint16_t* src = a.x + ml[u].row * a.ldx + ml[u].cb * kBlock + w.off;
+            xv[u][0] = ml[u].in ? ld16(src) : u32x4{};
+            xv[u][1] = ml[u].in ? ld16(src + 8) : u32x4{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float f[8];
-            if constexpr (F16)
-                unpack_f16x8(xv[u], f);
-            else
-                unpack_bf16x8(xv[u], f);
+            float f[16];
+            if constexpr (F16) {
+                unpack_f16x8(xv[u][0], f);
+                unpack_f16x8(xv[u][1], f + 8);
+            } else {
+                unpack_bf16x8(xv[u][0], f);
+                unpack_bf16x8(xv[u][1], f + 8);
+            }
             float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
                 m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-            const uint32_t amax_bits = quad_max4(__float_as_uint(m));
+            const uint32_t amax_bits = pair_max2(__float_as_uint(m));
             const uint32_t byte = F16 ? e8m0_from_f32_amax(__uint_as_float(amax_bits))
                                       : e8m0_from_bf16_amax(amax_bits >> 16);
             const float inv = e8m0_inv_scale(byte);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
                 f[i] = f[i] * inv;                 // exact: a power of two
-            const u32x2 codes = e4m3x8(f);
-            // gather the 4 group bytes of this 128-column block into the row's first lane
-            const uint32_t word = byte | (dpp<0x104>(byte) << 8) | (dpp<0x108>(byte) << 16) |
-                                  (dpp<0x10C>(byte) << 24);
+            const u32x2 lo = e4m3x8(f), hi = e4m3x8(f + 8);
+            const uint32_t word = gather_e8m0_pairs(byte);
             if (ml[u].in) {
-                st8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off, codes);
-                if ((lane & 15) == 0)
+                st16(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off, u32x4{lo.x, lo.y, hi.x, hi.y});
+                if ((lane & 7) == 0)
                     *reinterpret_cast<uint32_t*>(a.e + ml[u].row * a.lds + ml[u].cb * 4) = word;
             }
         }
@@ -161,37 +184,41 @@ struct E4Args {
     int64_t nb;
 };
 
+// A lane holds 16 values (Walk16): the block's codes are one 16-byte store per lane.
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_e4m3_b128(E4Args a) {
     const uint16_t* __restrict__ x = a.x;
     uint8_t* __restrict__ v = a.v;
     float* __restrict__ s = a.s;
     const int64_t nb = a.nb;
-    const Walk w(U);
-    const bool leader = (threadIdx.x & 15) == 0;
-    const int64_t nt = (nb + kTileBlocks - 1) / kTileBlocks;
+    const Walk16 w(U);
+    const bool leader = (threadIdx.x & 7) == 0;
+    const int64_t nt = (nb + kTileBlocks16 - 1) / kTileBlocks16;
     for (int64_t t0 = w.first; t0 < nt; t0 += w.step) {
-        u32x4 xv[U];
+        u32x4 xv[U][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
-            xv[u] = (b < nb) ? ld16(x + b * kBlock + w.off) : u32x4{};
+            const int64_t b = (t0 + u) * kTileBlocks16 + w.sub;
+            xv[u][0] = (b < nb) ? ld16(x + b * kBlock + w.off) : u32x4{};
+            xv[u][1] = (b < nb) ? ld16(x + b * kBlock + w.off + 8) : u32x4{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t b = (t0 + u) * kTileBlocks + w.sub;
-            float f[8];
-            unpack_bf16x8(xv[u], f);
+            const int64_t b = (t0 + u) * kTileBlocks16 + w.sub;
+            float f[16];
+            unpack_bf16x8(xv[u][0], f);
+            unpack_bf16x8(xv[u][1], f + 8);
             float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
                 m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-            const float amax = __uint_as_float(row_max16(__float_as_uint(m)));
+            const float amax = __uint_as_float(half_row_max8(__float_as_uint(m)));
             const float sc = e4m3_block_scale(amax);
             // zero block: every byte 0x00 (negative zeros included)
-            const u32x2 codes = (sc == 0.0f) ? u32x2{} : e4m3_quot8(f, sc);
+            const u32x2 lo = (sc == 0.0f) ? u32x2{} : e4m3_quot8(f, sc);
+            const u32x2 hi = (sc == 0.0f) ? u32x2{} : e4m3_quot8(f + 8, sc);
             if (b < nb) {
-                st8(v + b * kBlock + w.off, codes);
+                st16(v + b * kBlock + w.off, u32x4{lo.x, lo.y, hi.x, hi.y});
                 if (leader)
                     s[b] = sc;
             }
@@ -239,8 +266,17 @@ unsigned groups_for(int64_t nb) {
     return (unsigned)(want < kMaxGroups ? want : kMaxGroups);
 }
 
-constexpr int kUMx = 2;
+template <int U>
+unsigned groups16_for(int64_t nb) {
+    const int64_t per_group = (int64_t)kWavesPerGroup * U * kTileBlocks16;
+    const int64_t want = (nb + per_group - 1) / per_group;
+    return (unsigned)(want < kMaxGroups ? want : kMaxGroups);
+}
+
+constexpr int kUMx = 2;        // dequantize (8 values per lane)
 constexpr int kUE4 = 2;
+constexpr int kUMxQ = 1;       // quantize (16 values per lane)
+constexpr int kUE4Q = 1;
 
 }  // namespace
 
@@ -256,10 +292,10 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
     a.lds = lds;
     a.nblocks = (uint32_t)(rows * (cols / kBlock));
     a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
-    const dim3 grid(groups_for<kUMx>(a.nblocks));
+    const dim3 grid(groups16_for<kUMxQ>(a.nblocks));
     if (f16)
-        return launch1(k_quant_mx<kUMx, true>, grid, dim3(kGroupThreads), stream, a);
-    return launch1(k_quant_mx<kUMx, false>, grid, dim3(kGroupThreads), stream, a);
+        return launch1(k_quant_mx<kUMxQ, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_mx<kUMxQ, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0, int64_t lds,
@@ -280,7 +316,7 @@ hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
 hipError_t launch_quant_e4m3_b128(const uint16_t* x, uint8_t* v, float* s, int64_t n,
                                   hipStream_t stream) {
     const E4Args a{x, v, s, n / kBlock};
-    return launch1(k_quant_e4m3_b128<kUE4>, dim3(groups_for<kUE4>(a.nb)), dim3(kGroupThreads),
+    return launch1(k_quant_e4m3_b128<kUE4Q>, dim3(groups16_for<kUE4Q>(a.nb)), dim3(kGroupThreads),
                    stream, a);
 }
 

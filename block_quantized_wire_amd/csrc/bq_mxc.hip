@@ -15,9 +15,11 @@
 //   owner step    the accumulate, its bf16 sum requantized, and the owner's copy
 //                 materialized from that payload.
 //
-// Lane layout of the INT8 kernels: 8 values per lane, one 128-value block per DPP row, so
-// a 32-value group is one quad of lanes (its amax takes two DPP steps) and the 4 E8M0
-// bytes of a block are gathered into the row's first lane and stored as one dword.
+// Lane layouts of the INT8 kernels.  Quantize and ring hop give a lane 16 values: a
+// 128-value block per half DPP row, a 32-value group per lane pair (its amax one DPP step),
+// the codes one 16-byte store per lane.  Dequantize and accumulate give it 8: a block per
+// DPP row, a group per quad (two DPP steps).  Either way the 4 E8M0 bytes of a block are
+// gathered into the block's first lane and stored as one dword.
 #include "bq_device.h"
 #include "bq_launch.h"
 
@@ -100,29 +102,36 @@ __device__ __forceinline__ void store_e8m0_word(uint8_t* p, uint32_t word) {
     __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(p));
 }
 
+// A lane holds 16 values (Lanes16): a group of 32 is a lane pair, and the block's codes
+// are one 16-byte store per lane.
 template <int U>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mxf(MxfQuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
     uint8_t* __restrict__ v = a.v[blockIdx.y];
     uint8_t* __restrict__ e = a.e[blockIdx.y];
-    const Lanes L(U);
-    const int64_t nt = tiles_of(a.nb);
+    const Lanes16 L(U);
+    const int64_t nt = tiles16_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
-        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
-        u32x4 xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            xv[u] = (L.blk(u) < left) ? ld16(x + b0 * kBlock + L.val(u)) : u32x4{};
+        const int64_t b0 = t0 * kTileBlocks16, left = a.nb - b0;   // uniform
+        u32x4 xv[U][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float f[8];
-            unpack_bf16x8(xv[u], f);
-            const uint32_t amax_bits = quad_max4(__float_as_uint(abs_max8(f)));
+            const bool in = L.blk(u) < left;
+            xv[u][0] = in ? ld16(x + b0 * kBlock + L.val(u)) : u32x4{};
+            xv[u][1] = in ? ld16(x + b0 * kBlock + L.val(u) + 8) : u32x4{};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[16];
+            unpack_bf16x8(xv[u][0], f);
+            unpack_bf16x8(xv[u][1], f + 8);
+            const float m = __builtin_fmaxf(abs_max8(f), abs_max8(f + 8));
+            const uint32_t amax_bits = pair_max2(__float_as_uint(m));
             const uint32_t byte = e8m0_from_bf16_amax(amax_bits >> 16);
-            const u32x2 codes = mx_encode8(f, byte);
-            const uint32_t word = gather_e8m0(byte);
+            const u32x2 lo = mx_encode8(f, byte), hi = mx_encode8(f + 8, byte);
+            const uint32_t word = gather_e8m0_pairs(byte);
             if (L.blk(u) < left) {
-                st8(v + b0 * kBlock + L.val(u), codes);
+                st16(v + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
                 if (L.leader)
                     store_e8m0_word(e + (b0 + L.blk(u)) * 4, word);
             }
@@ -170,34 +179,38 @@ __global__ __launch_bounds__(kGroupThreads) void k_ring_hop_mx(MxfHopArgs a) {
     const uint16_t* __restrict__ local = a.local[blockIdx.y];
     uint8_t* v_out = a.v_out[blockIdx.y];
     uint8_t* e_out = a.e_out[blockIdx.y];
-    const Lanes L(U);
-    const int64_t nt = tiles_of(a.nb);
+    const Lanes16 L(U);
+    const uint32_t grp = L.off >> 5;          // the lane's group within its block
+    const int64_t nt = tiles16_of(a.nb);
     for (int64_t t0 = L.first; t0 < nt; t0 += L.step) {
-        const int64_t b0 = t0 * kTileBlocks, left = a.nb - b0;   // uniform
-        u32x2 vv[U];
-        u32x4 lv[U];
+        const int64_t b0 = t0 * kTileBlocks16, left = a.nb - b0;   // uniform
+        u32x4 vv[U], lv[U][2];
         uint32_t ev[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool in = L.blk(u) < left;
-            vv[u] = in ? ld8(v_in + b0 * kBlock + L.val(u)) : u32x2{};
-            ev[u] = in ? (uint32_t)e_in[(b0 + L.blk(u)) * 4 + L.grp()] : 127u;
-            lv[u] = in ? ld16(local + b0 * kBlock + L.val(u)) : u32x4{};
+            vv[u] = in ? ld16(v_in + b0 * kBlock + L.val(u)) : u32x4{};
+            ev[u] = in ? (uint32_t)e_in[(b0 + L.blk(u)) * 4 + grp] : 127u;
+            lv[u][0] = in ? ld16(local + b0 * kBlock + L.val(u)) : u32x4{};
+            lv[u][1] = in ? ld16(local + b0 * kBlock + L.val(u) + 8) : u32x4{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float deq[8], loc[8], sum[8];
-            mx_decode8(vv[u], ev[u], deq);
-            unpack_bf16x8(lv[u], loc);
+            float deq[16], loc[16], sum[16];
+            mx_decode8(u32x2{vv[u].x, vv[u].y}, ev[u], deq);
+            mx_decode8(u32x2{vv[u].z, vv[u].w}, ev[u], deq + 8);
+            unpack_bf16x8(lv[u][0], loc);
+            unpack_bf16x8(lv[u][1], loc + 8);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
                 sum[i] = deq[i] + loc[i];
-            const float amax = __uint_as_float(quad_max4(__float_as_uint(abs_max8(sum))));
+            const float m = __builtin_fmaxf(abs_max8(sum), abs_max8(sum + 8));
+            const float amax = __uint_as_float(pair_max2(__float_as_uint(m)));
             const uint32_t byte = e8m0_from_f32_amax(amax);
-            const u32x2 codes = mx_encode8(sum, byte);
-            const uint32_t word = gather_e8m0(byte);
+            const u32x2 lo = mx_encode8(sum, byte), hi = mx_encode8(sum + 8, byte);
+            const uint32_t word = gather_e8m0_pairs(byte);
             if (L.blk(u) < left) {
-                st8(v_out + b0 * kBlock + L.val(u), codes);
+                st16(v_out + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
                 if (L.leader)
                     store_e8m0_word(e_out + (b0 + L.blk(u)) * 4, word);
             }
@@ -289,7 +302,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_accum_mx(MxfAccumArgs a) {
     }
 }
 
-constexpr int kUMxf = 2;
+constexpr int kUMxf = 2;    // dequantize, accumulate (8 values per lane)
+constexpr int kUMxfQ = 1;   // quantize, ring hop (16 values per lane)
 
 }  // namespace
 
@@ -302,7 +316,7 @@ hipError_t launch_quant(int count, const uint16_t* const* x, uint8_t* const* v,
         a.e[i] = e[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_quant_mxf<kUMxf>, grid_for<kUMxf>(a.nb, count), dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_mxf<kUMxfQ>, grid16_for<kUMxfQ>(a.nb, count), dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant(int count, const uint8_t* const* v, const uint8_t* const* e,
@@ -334,7 +348,7 @@ hipError_t launch_ring_hop(int count, const uint8_t* const* v_in, const uint8_t*
         a.e_out[i] = e_out[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_ring_hop_mx<kUMxf>, grid_for<kUMxf>(a.nb, count), dim3(kGroupThreads), stream,
+    return launch1(k_ring_hop_mx<kUMxfQ>, grid16_for<kUMxfQ>(a.nb, count), dim3(kGroupThreads), stream,
                    a);
 }
 
