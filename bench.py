@@ -59,16 +59,24 @@ B_MX = 256 + 128 + 4       # bf16 in; E4M3 + 4 E8M0 bytes out (per 128 values)
 B_E4M3 = 256 + 132
 
 
+def code_only(text: str) -> str:
+    """Source text without // comments, trailing blanks and blank lines (the device sources
+    hold no // inside string literals)."""
+    lines = (line.split("//", 1)[0].rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_digest() -> str:
-    """Digest of the device code (the .hip sources and the headers they include): the HBM
-    counters in profiles/ stay valid while it is unchanged; host-side validation may change."""
+    """Digest of the device code (the .hip sources and the headers they include, comments
+    left out): the HBM counters in profiles/ stay valid while it is unchanged; host-side
+    validation and comments may change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_wire_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if not name.endswith((".hip", ".h")):
             continue
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

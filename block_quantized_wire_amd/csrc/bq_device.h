@@ -1,9 +1,11 @@
 // bq_device.h -- device building blocks of the libblockq kernels (gfx950, wave64).
 //
-// Work layout shared by every kernel: a lane owns 8 consecutive values (one 16-byte
-// bf16 vector), 16 lanes (one DPP row) own one 128-value block, and a wave64 covers
-// a "tile" of 4 blocks = 512 values per step.  Per-block reductions therefore stay
-// inside one DPP row and never touch LDS.
+// Work layouts of the codec kernels.  Kernels that write bf16 give a lane 8 consecutive
+// values (one 16-byte bf16 vector): 16 lanes (one DPP row) own one 128-value block and a
+// wave64 covers a "tile" of 4 blocks = 512 values per step (Lanes).  Kernels that write
+// the one-byte side give a lane 16 values (one 16-byte payload vector): 8 lanes (half a
+// DPP row) own a block and a tile is 8 blocks (Lanes16).  Per-block reductions therefore
+// stay inside one DPP row and never touch LDS.
 //
 // Arithmetic follows the codec definitions bit for bit (IEEE binary32, round to
 // nearest even, no contraction -- the library is compiled with -ffp-contract=off and
@@ -326,9 +328,9 @@ __device__ __forceinline__ float e8m0_inv_scale(uint32_t byte) {
 
 // ---- lane walk -----------------------------------------------------------------------
 
-// Lane bookkeeping of the flat kernels (one 128-value block per DPP row): the lane's
-// block within a tile and its first value in that block.  Waves walk the tiles
-// grid-stride, U adjacent tiles per step, so a launch needs no more workgroups than
+// Lane bookkeeping of the flat kernels with 8 values per lane (one 128-value block per DPP
+// row): the lane's block within a tile and its first value in that block.  Waves walk the
+// tiles grid-stride, U adjacent tiles per step, so a launch needs no more workgroups than
 // the chip holds at once.
 // The wave index is read from the first lane, so the tile a wave works on is a uniform
 // (scalar) value: each access is a scalar base of the step plus a small 32-bit lane

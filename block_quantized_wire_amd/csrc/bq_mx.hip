@@ -67,7 +67,7 @@ __device__ __forceinline__ MxLane mx_lane(const MxArgs& a, int64_t tile, int sub
     return m;
 }
 
-// Grid-stride walk over tiles of 4 blocks, U adjacent tiles per wave step.
+// Grid-stride walk over tiles of 4 blocks (8 values per lane), U adjacent tiles per wave step.
 struct Walk {
     int sub, off;
     int64_t first, step;

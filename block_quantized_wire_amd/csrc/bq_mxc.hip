@@ -63,8 +63,8 @@ struct MxfAccumArgs {
     int64_t seg_n;            // values per segment
 };
 
-// The 4 E8M0 bytes of a block -- one per quad of its DPP row -- packed into a word in the
-// row's first lane, group 0 in byte 0.
+// The 4 E8M0 bytes of a block whose lanes hold 8 values -- one per quad of its DPP row --
+// packed into a word in the row's first lane, group 0 in byte 0.
 __device__ __forceinline__ uint32_t gather_e8m0(uint32_t byte) {
     return byte | (dpp<0x104>(byte) << 8) | (dpp<0x108>(byte) << 16) | (dpp<0x10C>(byte) << 24);
 }
