@@ -217,3 +217,59 @@ def test_random_mm_mx(seed):
     bq.bq_mm_mx(to_dev(xv), to_dev(xe), to_dev(wv), to_dev(we), y)
     sync()
     assert np.array_equal(host(y, np.uint16), want), "exact case differs"
+
+
+@pytest.mark.parametrize("nblocks", range(1, 18))
+def test_every_tile_residue(nblocks):
+    """1..17 blocks: every residue of the block count modulo the 8-block tiles of the
+    16-values-per-lane kernels (and the 4-block tiles of the others), for each kernel
+    that walks them: INT8 quantize and hop, E4M3-b128 quantize, MXFP8 flat quantize and
+    hop, 2-D MXFP8 quantize of one row; bit for bit, and nothing written past the end."""
+    import torch
+    rng = np.random.default_rng(5000 + nblocks)
+    n = 128 * nblocks
+    say(f"tile residues nblocks={nblocks}")
+    x, local = draw(rng, n, hi=60), draw(rng, n, hi=60)
+    pad = 4096                                         # canary bytes past the end
+    q = torch.full((n + pad,), 0x5A, dtype=torch.int8, device="cuda")
+    s = torch.full((n // 128 + 64,), -1.0, dtype=torch.float32, device="cuda")
+    bq.bq_quant_i8(to_dev(x), q, s, n=n)
+    sync()
+    wq, ws = oracle.quant_i8(x)
+    assert_same(host(q, np.int8)[:n], wq, "INT8 payload")
+    assert_same(host(s, np.float32)[:n // 128], ws, "INT8 scales")
+    assert bool((q[n:] == 0x5A).all()) and bool((s[n // 128:] == -1.0).all()), "INT8 wrote past n"
+    bq.bq_ring_hop_i8(q, s, to_dev(local), q, s, n=n)
+    sync()
+    hq, hs = oracle.ring_hop_i8(wq, ws, local)
+    assert_same(host(q, np.int8)[:n], hq, "hop payload")
+    assert_same(host(s, np.float32)[:n // 128], hs, "hop scales")
+    assert bool((q[n:] == 0x5A).all()) and bool((s[n // 128:] == -1.0).all()), "hop wrote past n"
+    v = torch.full((n + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    es = torch.full((n // 128 + 64,), -1.0, dtype=torch.float32, device="cuda")
+    bq.bq_quant_e4m3_b128(to_dev(x), v, es, n=n)
+    sync()
+    wv, wes = oracle.quant_e4m3_b128(x)
+    assert_same(host(v, np.uint8)[:n], wv, "E4M3-b128 values")
+    assert_same(host(es, np.float32)[:n // 128], wes, "E4M3-b128 scales")
+    assert bool((v[n:] == 0xA5).all()), "E4M3-b128 wrote past n"
+    e = torch.full((n // 32 + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    bq.bq_quant_mx_batch([to_dev(x)], [v], [e], n=n)
+    sync()
+    fv, fe = oracle.quant_mx_flat(x)
+    assert_same(host(v, np.uint8)[:n], fv, "MX flat codes")
+    assert_same(host(e, np.uint8)[:n // 32], fe, "MX flat scales")
+    assert bool((v[n:] == 0xA5).all()) and bool((e[n // 32:] == 0xA5).all()), "MX wrote past n"
+    bq.bq_ring_hop_mx(v, e, to_dev(local), v, e, n=n)
+    sync()
+    hv, he = oracle.ring_hop_mx(fv, fe, local)
+    assert_same(host(v, np.uint8)[:n], hv, "MX hop codes")
+    assert_same(host(e, np.uint8)[:n // 32], he, "MX hop scales")
+    assert bool((v[n:] == 0xA5).all()) and bool((e[n // 32:] == 0xA5).all()), "MX hop wrote past n"
+    v2 = torch.full((1, n + 128), 0xA5, dtype=torch.uint8, device="cuda")
+    e2 = torch.full((1, n // 32 + 4), 0xA5, dtype=torch.uint8, device="cuda")
+    bq.bq_quant_mx(to_dev(x.reshape(1, n)), v2, e2, rows=1, cols=n)
+    sync()
+    assert_same(host(v2, np.uint8)[0, :n], fv, "MX 2-D codes")
+    assert_same(host(e2, np.uint8)[0, :n // 32], fe, "MX 2-D scales")
+    assert bool((v2[0, n:] == 0xA5).all()) and bool((e2[0, n // 32:] == 0xA5).all()), "MX 2-D wrote past cols"
