@@ -28,6 +28,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -44,6 +45,7 @@ N = ROWS * COLS
 NB = N // 128
 M = N // W                 # values per ring chunk / A2A shard
 SETS = 4                   # rotating buffer sets, each a full step's inputs and outputs (~1 GB)
+SAMPLES = 5                # timed samples per kernel in timed region 2 (median reported)
 
 # algorithmic bytes per 128 values of each kernel (inputs read once, outputs written once)
 B_QUANT = 256 + 132        # bf16 in; int8 + fp32 scale out
@@ -299,6 +301,30 @@ def copy_reference(torch, stream, total_bytes: int, reps: int) -> dict:
             "gbs": round(2 * half / (us * 1e-6) / 1e9, 1)}
 
 
+def receipt(torch, bq) -> dict:
+    """What the figures were measured on: software versions and the device."""
+    props = torch.cuda.get_device_properties(0)
+    out = {"torch": torch.__version__, "hip": torch.version.hip, "library": bq.bq_version(),
+           "device": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
+           "memory_gib": round(props.total_memory / 2 ** 30, 1)}
+    uuid = getattr(props, "uuid", None)
+    if uuid is not None:
+        out["uuid"] = str(uuid)
+    return out
+
+
+def cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(rows_per_rank: int) -> dict:
     """The oracle, single-threaded, on the first `rows_per_rank` rows of every rank."""
     import oracle
@@ -419,31 +445,37 @@ def main() -> int:
     # rotating over the buffer sets (inputs and outputs: consecutive launches share no
     # buffer, so inputs are cold in the last-level cache) between one pair of HIP events
     # on the launch stream -- no event sits between two launches, so the average is
-    # the kernel's own duration as a trace shows it.
+    # the kernel's own duration as a trace shows it.  SAMPLES such samples per kernel,
+    # taken round-robin over the kernels; the figure is their median.
     reps = max(10, args.steps // 4)
 
     def time_kinds(seqs):
         kinds = {}
         for k, (name, nbytes, _, _) in enumerate(seqs[0]):
             kinds.setdefault((name, nbytes), []).append(k)
+        samples = {key: [] for key in kinds}
+        for smp in range(SAMPLES):
+            for (name, nbytes), idx in kinds.items():
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(step.stream)
+                for i in range(smp * reps, (smp + 1) * reps):
+                    _, _, fn, fargs = seqs[i % len(seqs)][idx[i % len(idx)]]
+                    st = fn(*fargs)
+                    if st != 0:
+                        raise RuntimeError(f"{name}: status {st}")
+                e1.record(step.stream)
+                torch.cuda.synchronize()
+                samples[(name, nbytes)].append(e0.elapsed_time(e1) * 1e3 / reps)
         out = {}
         for (name, nbytes), idx in kinds.items():
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(step.stream)
-            for i in range(reps):
-                _, _, fn, fargs = seqs[i % len(seqs)][idx[i % len(idx)]]
-                st = fn(*fargs)
-                if st != 0:
-                    raise RuntimeError(f"{name}: status {st}")
-            e1.record(step.stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            us = statistics.median(samples[(name, nbytes)])
             gbs = nbytes / (us * 1e-6) / 1e9
             out[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_step": len(idx),
                                            "us_per_launch": us, "gbs": gbs,
-                                           "frac": gbs / HBM_PEAK_GBS, "us_per_step": us * len(idx)}
+                                           "frac": gbs / HBM_PEAK_GBS, "us_per_step": us * len(idx),
+                                           "samples_us": [round(t, 2) for t in samples[(name, nbytes)]]}
         return out
 
     per = time_kinds(step.kernels)
@@ -525,16 +557,19 @@ def main() -> int:
         "kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
                         "launches_per_step": v["launches_per_step"],
                         "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
-                        "frac": round(v["frac"], 4)} for k, v in per.items()},
+                        "frac": round(v["frac"], 4), "samples_us": v["samples_us"]}
+                    for k, v in per.items()},
         # the MXFP8 ring / all-to-all primitives at the same shapes, timed the same way;
         # not part of the step and not in `value`
         "next_kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
                              "launches_per_pass": v["launches_per_step"],
                              "us_per_launch": round(v["us_per_launch"], 2),
-                             "gbs": round(v["gbs"], 1), "frac": round(v["frac"], 4)}
+                             "gbs": round(v["gbs"], 1), "frac": round(v["frac"], 4),
+                             "samples_us": v["samples_us"]}
                          for k, v in per_next.items()},
     }
     line["accuracy"] = accuracy
+    line["receipt"] = receipt(torch, bq)
     line["gemm"] = gemm_bench(torch, bq, reps=10)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_rows)
@@ -543,7 +578,7 @@ def main() -> int:
         ca = cpu_baseline_all_cores(nw)
         all_gbs = step.step_bytes / ca["seconds"] / 1e9
         line["cpu_baseline"] = {"value": round(all_gbs, 4), "unit": "GB/s", "cores": ca["workers"],
-                                "kind": "oracle",
+                                "kind": "oracle", "cpu": cpu_model(),
                                 "sample": f"the whole step (all {ROWS} rows of every rank), the rows "
                                           f"of each chunk split over {ca['workers']} processes "
                                           f"({ca['seconds']:.2f} s)",
