@@ -48,3 +48,11 @@ def test_bench_line_fields():
     assert g["bound"] == "mfma" and g["unit"] == "TFLOP/s" and g["peak"] == 5000.0
     assert abs(g["frac"] - g["achieved"] / g["peak"]) < 1e-3
     assert d["accuracy"]["ranks_bit_identical"] is True
+    # per-kernel figures are medians of their samples
+    import statistics
+    for k, v in d["kernels"].items():
+        assert len(v["samples_us"]) == 5, k
+        assert abs(statistics.median(v["samples_us"]) - v["us_per_launch"]) <= 0.011, k
+    for k in ("torch", "hip", "library", "device", "arch", "compute_units", "memory_gib"):
+        assert k in d["receipt"], k
+    assert "gfx950" in d["receipt"]["arch"]
