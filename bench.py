@@ -259,19 +259,22 @@ def gemm_bench(torch, bq, reps: int) -> dict:
         bq.bq_mm_mx(xv, xe, wv, we, y)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        bq.bq_mm_mx(xv, xe, wv, we, y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    samples = []
+    for _ in range(SAMPLES):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            bq.bq_mm_mx(xv, xe, wv, we, y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = statistics.median(samples)
     flops = 2.0 * MM_M * MM_N * K
     tflops = flops / (us * 1e-6) / 1e12
     return {"workload": f"staged MXFP8 GEMM {MM_M}x{MM_N}x{K} (six 4096x7168 slices), bf16 out",
             "bound": "mfma", "us_per_launch": round(us, 1), "achieved": round(tflops, 1),
             "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-            "flops_per_launch": flops}
+            "flops_per_launch": flops, "samples_us": [round(t, 1) for t in samples]}
 
 
 def copy_reference(torch, stream, total_bytes: int, reps: int) -> dict:
@@ -570,7 +573,7 @@ def main() -> int:
     }
     line["accuracy"] = accuracy
     line["receipt"] = receipt(torch, bq)
-    line["gemm"] = gemm_bench(torch, bq, reps=10)
+    line["gemm"] = gemm_bench(torch, bq, reps=4)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_rows)
         cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9
