@@ -236,7 +236,7 @@ MM_M, MM_N, MM_SLICES = 4096, 7168, 6      # staged projection: six 4096 x 7168 
 MFMA_FP8_PEAK_TFLOPS = 5000.0               # MI355X dense fp8 matrix-core peak
 
 
-def gemm_bench(torch, bq, reps: int) -> dict:
+def gemm_bench(torch, bq, reps: int, warmup: int = 2) -> dict:
     """The dense MXFP8 GEMM from a staged buffer (not part of the step): six bf16 slices
     of 4096 x 7168 quantized into a 4096 x 43008 staging buffer, times 7168 x 43008 MXFP8
     weights, into bf16.  Synthetic N(0, 1) inputs drawn on the GPU with a fixed seed."""
@@ -255,7 +255,7 @@ def gemm_bench(torch, bq, reps: int) -> dict:
     del w
     y = torch.empty((MM_M, MM_N), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(2):
+    for _ in range(warmup):
         bq.bq_mm_mx(xv, xe, wv, we, y)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -573,7 +573,7 @@ def main() -> int:
     }
     line["accuracy"] = accuracy
     line["receipt"] = receipt(torch, bq)
-    line["gemm"] = gemm_bench(torch, bq, reps=4)
+    line["gemm"] = gemm_bench(torch, bq, reps=4, warmup=20)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_rows)
         cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9
