@@ -53,7 +53,25 @@ MUTANTS = [
     ("MX hop rounds the sums to bf16 first", "            sums[i] = dq + lp;",
      "            sums[i] = orc_bf16_to_f32(orc_f32_to_bf16(dq + lp));",
      ["test_mx_ring_hop_bruteforce_and_identities"]),
-    ("binary16 exponent bias off by one", "ldexpf((float)(1024 + man), ex - 25)",
+    ("INT8 hop rounds the sums to bf16 first", "            sum[i] = deq + loc;",
+     "            sum[i] = orc_bf16_to_f32(orc_f32_to_bf16(deq + loc));",
+     ["test_ring_hop_bruteforce_and_identities"]),
+    ("A2A accumulate fuses multiply and add",
+     "            float term = (float)q[s][i] * scale[s][i / BLK];\n            acc = acc + term;",
+     "            acc = fmaf((float)q[s][i], scale[s][i / BLK], acc);",
+     ["test_accum_respects_array_order_and_rounds_each_product"]),
+    ("materialization truncates to bf16",
+     "        float v = (float)q[i] * scale[i / BLK];\n        y[i] = orc_f32_to_bf16(v);",
+     "        float v = (float)q[i] * scale[i / BLK];\n"
+     "        { uint32_t u_; memcpy(&u_, &v, 4); y[i] = (uint16_t)(u_ >> 16); }",
+     ["test_i8_dequant_matches_torch_products"]),
+    ("E4M3-b128 zero block stores scale 1", "            scale[b] = 0.0f;", "            scale[b] = 1.0f;",
+     ["test_e4m3_b128_worked_examples"]),
+    ("A2A owner materializes from its bf16 sum, not the payload",
+     "            orc_dequant_i8(q_out + j * seg_n, s_out + j * sb, seg_n, y_out[j]);",
+     "            memcpy(y_out[j], sum, (size_t)seg_n * sizeof(uint16_t));",
+     ["test_a2a_reduce_is_accumulate_then_quantize_then_materialize"]),
+    ("binary16 exponent bias off by one","ldexpf((float)(1024 + man), ex - 25)",
      "ldexpf((float)(1024 + man), ex - 24)", ["test_f16_decode_exhaustive_matches_numpy"]),
     ("binary16 subnormal step 2^-23", "ldexpf((float)man, -24)", "ldexpf((float)man, -23)",
      ["test_f16_decode_exhaustive_matches_numpy"]),

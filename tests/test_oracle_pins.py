@@ -280,13 +280,18 @@ def test_accum_respects_array_order_and_rounds_each_product():
     q[2][0], s[2][0] = 1, 2.0 ** -10
     assert oracle.dequant_accum_i8(q, s)[0] == 0x3A80                            # 2^-10
     assert oracle.dequant_accum_i8([q[0], q[2], q[1]], [s[0], s[2], s[1]])[0] == 0  # absorbed
-    # product rounding: 3 * (1 + 2^-23) = 3 + 3*2^-23 rounds to 3 + 2^-21 (tie to even);
-    # adding -3 then leaves exactly 2^-21, while a fused multiply-add would leave 3*2^-23.
+    # product rounding: 3 * (1 + 2^-23) = 3 + 3*2^-23 rounds to 3 + 2^-21 (tie to even),
+    # so the sum with -3 is exactly 2^-21 in either order.
     q2 = [np.zeros(n, np.int8), np.zeros(n, np.int8)]
     s2 = [np.array([np.float32(1 + 2.0 ** -23)], np.float32), np.array([1.0], np.float32)]
     q2[0][0], q2[1][0] = 3, -3
     got = oracle.dequant_accum_i8(q2, s2)[0]
     assert got == bf.fraction_to_bf16_bits(Fraction(2) ** -21)
+    # With the rounded product second, a fused multiply-add onto acc = -3 would keep the
+    # exact 3*2^-23 instead.  Onto acc = +0, as above, fusing rounds like the product.
+    got = oracle.dequant_accum_i8(q2[::-1], s2[::-1])[0]
+    assert got == bf.fraction_to_bf16_bits(Fraction(2) ** -21)
+    assert got != bf.fraction_to_bf16_bits(3 * Fraction(2) ** -23)
     # brute force on random small cases
     rng = np.random.default_rng(4)
     for W in (1, 2, 3):
