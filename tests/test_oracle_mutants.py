@@ -56,6 +56,12 @@ MUTANTS = [
     ("INT8 hop rounds the sums to bf16 first", "            sum[i] = deq + loc;",
      "            sum[i] = orc_bf16_to_f32(orc_f32_to_bf16(deq + loc));",
      ["test_ring_hop_bruteforce_and_identities"]),
+    ("INT8 hop fuses the dequantize into the add",
+     "            float deq = (float)q_in[b * BLK + i] * s_in[b];\n"
+     "            float loc = orc_bf16_to_f32(local[b * BLK + i]);\n            sum[i] = deq + loc;",
+     "            float loc = orc_bf16_to_f32(local[b * BLK + i]);\n"
+     "            sum[i] = fmaf((float)q_in[b * BLK + i], s_in[b], loc);",
+     ["test_ring_hop_bruteforce_and_identities"]),
     ("A2A accumulate fuses multiply and add",
      "            float term = (float)q[s][i] * scale[s][i / BLK];\n            acc = acc + term;",
      "            acc = fmaf((float)q[s][i], scale[s][i / BLK], acc);",
