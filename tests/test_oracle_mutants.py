@@ -31,6 +31,9 @@ MUTANTS = [
      ["test_accum_respects_array_order_and_rounds_each_product"]),
     ("E8M0 rounds an exact power of two up", "int e = (f == 0.5f) ? k - 1 : k;", "int e = k;",
      ["test_mx_worked_examples"]),
+    ("E8M0 by the OCP floor rule, floor(log2 amax) - 8", "    int e = (f == 0.5f) ? k - 1 : k;",
+     "    int e = k; { int ka; (void)frexpf(amax, &ka); e = ka - 9; (void)f; }",
+     ["test_mx_worked_examples", "test_e8m0_exhaustive_over_bf16_amax"]),
     ("E4M3 ties always upward", "code = (lo % 2 == 0) ? lo : hi;", "code = hi;",
      ["test_e4m3_encode_midpoints_and_random_fp32"]),
     ("hop subtracts the local partial", "sum[i] = deq + loc;", "sum[i] = deq - loc;",
