@@ -76,6 +76,19 @@ MUTANTS = [
      ["test_i8_dequant_matches_torch_products"]),
     ("E4M3-b128 zero block stores scale 1", "            scale[b] = 0.0f;", "            scale[b] = 1.0f;",
      ["test_e4m3_b128_worked_examples"]),
+    ("A2A requantizes the binary32 sum, not the bf16 sum",
+     "        orc_quant_i8(red + j * m, m, q_final + j * m, s_final + j * mb);",
+     "        for (int64_t b = 0; b < mb; b++) {\n"
+     "            float f32s[BLK];\n"
+     "            for (int i = 0; i < BLK; i++) {\n"
+     "                float acc = 0.0f;\n"
+     "                for (int k = 0; k < W; k++)\n"
+     "                    acc = acc + (float)qp[k][b * BLK + i] * sp[k][b];\n"
+     "                f32s[i] = acc;\n"
+     "            }\n"
+     "            quant_block_f32(f32s, q_final + j * m + b * BLK, s_final + j * mb + b);\n"
+     "        }",
+     ["test_a2a_requantizes_the_bf16_sum"]),
     ("A2A owner materializes from its bf16 sum, not the payload",
      "            orc_dequant_i8(q_out + j * seg_n, s_out + j * sb, seg_n, y_out[j]);",
      "            memcpy(y_out[j], sum, (size_t)seg_n * sizeof(uint16_t));",
