@@ -89,6 +89,19 @@ MUTANTS = [
      "            quant_block_f32(f32s, q_final + j * m + b * BLK, s_final + j * mb + b);\n"
      "        }",
      ["test_a2a_requantizes_the_bf16_sum"]),
+    ("MX A2A requantizes the binary32 sum, not the bf16 sum",
+     "        quant_mx_flat(red + j * m, m, v_final + j * m, e_final + j * mg);",
+     "        for (int64_t g = 0; g < mg; g++) {\n"
+     "            float f32s[MXG];\n"
+     "            for (int i = 0; i < MXG; i++) {\n"
+     "                float acc = 0.0f;\n"
+     "                for (int r = 0; r < W; r++)\n"
+     "                    acc = acc + mx_value(vp[r][g * MXG + i], ep[r][g]);\n"
+     "                f32s[i] = acc;\n"
+     "            }\n"
+     "            quant_group_mx(f32s, v_final + j * m + g * MXG, e_final + j * mg + g);\n"
+     "        }",
+     ["test_mx_a2a_reduce_is_accumulate_then_quantize_then_materialize"]),
     ("A2A owner materializes from its bf16 sum, not the payload",
      "            orc_dequant_i8(q_out + j * seg_n, s_out + j * sb, seg_n, y_out[j]);",
      "            memcpy(y_out[j], sum, (size_t)seg_n * sizeof(uint16_t));",
