@@ -74,10 +74,6 @@ def fraction_to_bf16_bits(v: Fraction) -> int:
     return sign | ((e + 127) << 7) | man
 
 
-def f32_to_fraction(f) -> Fraction:
-    return Fraction(float(np.float32(f)))
-
-
 def nearest_int_even(t: Fraction, lo: int, hi: int) -> int:
     """argmin over k in [lo, hi] of |t - k|, ties to the even k."""
     best = None
