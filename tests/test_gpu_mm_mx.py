@@ -113,6 +113,37 @@ def test_mm_mx_exact_small_integers(M, N, K):
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("M,N,K", [(130, 272, 384), (257, 129, 640)])
+def test_mm_mx_padded_strides_match_dense(M, N, K):
+    """Every leading dimension padded: values by multiples of 16 bytes, scales by multiples
+    of 4, the output by an odd count.  The value padding holds the E4M3 NaN code and the
+    scale padding the E8M0 NaN byte, so a read past a row's K columns would show.  The
+    result equals the dense-stride launch bit for bit, and the output padding is untouched."""
+    say(f"mm_mx padded strides {M}x{N}x{K}")
+    x = workloads.rows(4, 3, 0, M, K)
+    w = workloads.rows(6, 4, 0, N, K)
+    xv, xe = oracle.quant_mx(x)
+    wv, we = oracle.quant_mx(w)
+    dense = gpu_mm(xv, xe, wv, we, M, N, K)
+
+    def padded(a, extra, byte):
+        buf = filled((a.shape[0], a.shape[1] + extra), np.uint8, byte)
+        buf[:, :a.shape[1]].copy_(to_dev(a))
+        return buf[:, :a.shape[1]]
+
+    xvp, wvp = padded(xv, 256, 0x7F), padded(wv, 48, 0xFF)
+    xep, wep = padded(xe, 12, 0xFF), padded(we, 4, 0xFF)
+    assert xvp.stride(0) == K + 256 and wep.stride(0) == K // 32 + 4
+    y = filled((M, N + 13), np.uint16, 0x5A)
+    bq.bq_mm_mx(xvp, xep, wvp, wep, y[:, :N], M=M, N=N, K=K)
+    sync()
+    got = host(y, np.uint16)
+    assert np.array_equal(got[:, :N], dense), "padded strides change the result"
+    assert np.all(got[:, N:] == 0x5A5A), "wrote into the output padding"
+    Y, S = oracle.mm_mx(xv, xe, wv, we)
+    check_close(got[:, :N], Y, S, block_max_sum(xv, xe, wv, we), K, "outputs")
+
+
 def test_mm_mx_staged_full_size_sampled():
     """The staged projection geometry: six 4096x7168 bf16 slices quantized into a 4096 x
     43008 staging buffer, times 7168 x 43008 MXFP8 weights.  The GEMM of the staged buffer
