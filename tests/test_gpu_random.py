@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import empty, host, say, sync, to_dev
+from gpu_util import empty, filled, host, say, sync, to_dev
 
 from block_quantized_wire_amd import build as _build
 
@@ -138,22 +138,31 @@ def test_random_mx_and_e4m3(seed):
     fmt = "f16" if rng.integers(0, 2) else "bf16"
     n = blocks(rng)
     nsrc = int(rng.integers(1, 65))
-    say(f"random mx seed={seed} {fmt} {rows}x{cols} pads=({padv},{pads}); flat n={n} "
-        f"nsrc={nsrc}; e4m3-b128")
-    # 2-D MXFP8 with padded strides (binary16 input: magnitudes within its range)
+    # input and output row padding from a generator of their own, so the draws above and
+    # below are the same as without it
+    prng = np.random.default_rng(5000 + seed)
+    padx, pady = 8 * int(prng.integers(0, 3)), 8 * int(prng.integers(0, 3))
+    say(f"random mx seed={seed} {fmt} {rows}x{cols} pads=({padv},{pads}) ldx pad {padx} "
+        f"ldy pad {pady}; flat n={n} nsrc={nsrc}; e4m3-b128")
+    # 2-D MXFP8 with padded strides (binary16 input: magnitudes within its range).  The input
+    # padding holds NaN bit patterns, so reading it would corrupt a group's scale.
     x = draw(rng, rows * cols, lo=-20, hi=14, fmt=fmt) if fmt == "f16" else draw(rng, rows * cols)
     x = x.reshape(rows, cols)
+    xbuf = filled((rows, cols + padx), np.uint16, 0xFF)
+    xbuf[:, :cols].copy_(to_dev(x))
     ldv, lds = cols + padv, cols // 32 + pads
     v, e = empty((rows, ldv), np.uint8), empty((rows, lds), np.uint8)
     quant = bq.bq_quant_mx_f16 if fmt == "f16" else bq.bq_quant_mx
-    quant(to_dev(x), v, e, rows=rows, cols=cols, ldv=ldv, lds=lds)
-    y = empty((rows, cols), np.uint16)
-    bq.bq_dequant_mx(v, e, y, rows=rows, cols=cols, ldv=ldv, lds=lds)
+    quant(xbuf[:, :cols], v, e, rows=rows, cols=cols, ldx=cols + padx, ldv=ldv, lds=lds)
+    ybuf = filled((rows, cols + pady), np.uint16, 0xA5)
+    bq.bq_dequant_mx(v, e, ybuf[:, :cols], rows=rows, cols=cols, ldv=ldv, lds=lds, ldy=cols + pady)
     sync()
     wv, we = oracle.quant_mx_f16(x) if fmt == "f16" else oracle.quant_mx(x)
     assert_same(host(v, np.uint8)[:, :cols], wv, "E4M3 values")
     assert_same(host(e, np.uint8)[:, :cols // 32], we, "E8M0 scales")
-    assert_same(host(y, np.uint16), oracle.dequant_mx(wv, we), "MX bf16")
+    y = host(ybuf, np.uint16)
+    assert_same(y[:, :cols], oracle.dequant_mx(wv, we), "MX bf16")
+    assert np.all(y[:, cols:] == 0xA5A5), "dequantize wrote into the row padding"
     # flat MXFP8: hop in place, accumulate
     xf = draw(rng, n, hi=80)
     fv, fe = oracle.quant_mx_flat(xf)
