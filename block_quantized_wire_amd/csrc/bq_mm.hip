@@ -18,13 +18,20 @@
 // SIMD, so one can issue matrix instructions while the other waits on LDS) own 128 x 64
 // pieces, each 8 x 4 MFMA blocks: a wave reads 12 operand fragments from LDS per 32
 // MFMAs.
-// Per K step of 128 the workgroup stages the X and W tiles (32 KB each) and their
-// 256 x 4 scale bytes in LDS, double-buffered (132 KB), with gfx950's global-to-LDS
+// Per K step of 128 the workgroup stages the X and W tiles (32 KB each) in LDS,
+// double-buffered, with gfx950's global-to-LDS
 // loads (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane i at
 // byte 16i), so no registers hold the staged data and the loads of step k+1 are in
 // flight while step k computes; one barrier per step.  A tile row is 128 contiguous
 // bytes; its 16-byte chunk c sits in slot c ^ ((row >> 1) & 7), so the 16 rows a
 // fragment read touches at one chunk fall in 16 distinct 16-byte bank groups.
+//
+// Scales: a row's E8M0 bytes for one K step are 4 bytes, and fetching them as their own
+// 4-byte request per row and step cost about 11% of the kernel's time (one request per row
+// beside the row's two 64-byte operand requests).  When K is a multiple of 512 and the scale
+// rows are 16-byte aligned, one 16-byte load per row brings the scales of 4 K steps into a
+// double-buffered LDS area (2 x 8 KB), a quarter of the requests; otherwise each step stages
+// its rows' 4 bytes with its operands.
 //
 // Tiles are handed out column-major, each XCD (every 8th workgroup) taking a contiguous
 // run: an XCD works through a band of W columns, whose tiles all its workgroups re-read
@@ -47,6 +54,8 @@ constexpr int kWavesN = kTN / kWN;                // wave grid: (kTM / kWM) x kW
 constexpr int kFA = kWM / 16, kFB = kWN / 16;     // MFMA blocks per wave tile side
 constexpr int kWaveLoads = kTM * kTK / 1024 / kWaves;   // 1 KB loads per wave per operand
 constexpr int kScaleRows = kTM / kWaves;                 // scale rows per wave per operand
+constexpr int kGroupSteps = 4;                           // K steps per grouped scale load
+constexpr int kScaleSlots = kTM + kTN;                   // X rows, then W rows
 
 struct MmArgs {
     const uint8_t* xv;
@@ -67,6 +76,13 @@ struct Stage {
     uint32_t sc[kTM + kTN];
 };
 
+struct Smem {
+    Stage stage[2];
+    // grouped scales: slot r (X row r, then W row r - kTM) holds the 16 E8M0 bytes of
+    // kGroupSteps K steps, word j for step j of the group
+    uint32_t scg[2][kScaleSlots * kGroupSteps];
+};
+
 __device__ __forceinline__ uint32_t x_scale_word(const Stage& st, int row) {
     return st.sc[(row / kScaleRows) * 64 + row % kScaleRows];
 }
@@ -78,9 +94,10 @@ __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 
 
 // Issue the global-to-LDS loads of one K step into `st`: wave w fills 1 KB pieces
 // w*kWaveLoads .. of each operand (64 lanes x 16 bytes; lane i lands at byte 16i of the
-// piece and fetches the chunk that belongs in that slot), and the scale words of X and W
-// rows [32w, 32w+32) (4 bytes per lane: lanes 0-31 X, 32-63 W).  Rows beyond M (N) are clamped to the last row; their
+// piece and fetches the chunk that belongs in that slot), and, in the per-step form, the
+// scale words of X and W rows [32w, 32w+32) (4 bytes per lane: lanes 0-31 X, 32-63 W).  Rows beyond M (N) are clamped to the last row; their
 // results are never stored.
+template <bool Grouped>
 __device__ __forceinline__ void load_step(const MmArgs& p, Stage& st, int m0, int n0, int k0,
                                           int wave, int lane) {
 #pragma unroll
@@ -95,11 +112,25 @@ __device__ __forceinline__ void load_step(const MmArgs& p, Stage& st, int m0, in
         __builtin_amdgcn_global_load_lds(p.wv + (int64_t)nb * p.ldwv + k0 + 16 * c,
                                          st.b + piece * 1024, 16, 0, 0);
     }
+    if (Grouped)
+        return;
     const int r = kScaleRows * wave + (lane & 31);
     const uint8_t* src = lane < 32
         ? p.xe + (int64_t)min(m0 + r, p.M - 1) * p.ldxe + k0 / 32
         : p.we + (int64_t)min(n0 + r, p.N - 1) * p.ldwe + k0 / 32;
     __builtin_amdgcn_global_load_lds(src, st.sc + 64 * wave, 4, 0, 0);
+}
+
+// The scales of K steps [4g, 4g+4), bytes [16g, 16g+16) of every E8M0 row, into `dst`:
+// wave w fills slots [64w, 64w+64) (X rows for w < 4, W rows after), 16 bytes per lane,
+// lane i at slot 64w + i.  Rows beyond M (N) are clamped to the last row.
+__device__ __forceinline__ void load_scale_group(const MmArgs& p, uint32_t* dst, int m0, int n0,
+                                                 int g, int wave, int lane) {
+    const int slot = 64 * wave + lane;
+    const uint8_t* src = slot < kTM
+        ? p.xe + (int64_t)min(m0 + slot, p.M - 1) * p.ldxe + 16 * g
+        : p.we + (int64_t)min(n0 + slot - kTM, p.N - 1) * p.ldwe + 16 * g;
+    __builtin_amdgcn_global_load_lds(src, dst + 64 * kGroupSteps * wave, 16, 0, 0);
 }
 
 // Wait for this wave's global-to-LDS loads (the barrier that follows publishes them).
@@ -122,8 +153,10 @@ __device__ __forceinline__ int tile_of(int bid, int tiles) {
     return (bid % 8) * (tiles / 8) + bid / 8;
 }
 
+template <bool Grouped>
 __global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
-    __shared__ Stage stage[2];
+    __shared__ Smem sm;
+    Stage* stage = sm.stage;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,27 +173,37 @@ __global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
             acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = p.K / kTK;
-    load_step(p, stage[0], m0, n0, 0, wave, lane);
+    load_step<Grouped>(p, stage[0], m0, n0, 0, wave, lane);
+    if (Grouped)
+        load_scale_group(p, sm.scg[0], m0, n0, 0, wave, lane);
     wait_loads();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more)
-            load_step(p, stage[(kt + 1) & 1], m0, n0, (kt + 1) * kTK, wave, lane);
+            load_step<Grouped>(p, stage[(kt + 1) & 1], m0, n0, (kt + 1) * kTK, wave, lane);
+        // the next group's scales go into the buffer the previous group used; they land by
+        // this step's closing wait, three steps before they are read
+        if (Grouped && (kt & (kGroupSteps - 1)) == 0 && kt + kGroupSteps < nk)
+            load_scale_group(p, sm.scg[(kt / kGroupSteps + 1) & 1], m0, n0, kt / kGroupSteps + 1,
+                             wave, lane);
         const Stage& st = stage[kt & 1];
+        const uint32_t* scg = sm.scg[(kt / kGroupSteps) & 1] + (kt & (kGroupSteps - 1));
         i32x8 bf[kFB];
         int bsc[kFB];
 #pragma unroll
         for (int b = 0; b < kFB; ++b) {
             const int n = wn + 16 * b + r16;
             bf[b] = frag(st.b, n, g);
-            bsc[b] = (int)((w_scale_word(st, n) >> (8 * g)) & 0xFFu);
+            const uint32_t ww = Grouped ? scg[(kTM + n) * kGroupSteps] : w_scale_word(st, n);
+            bsc[b] = (int)((ww >> (8 * g)) & 0xFFu);
         }
 #pragma unroll
         for (int a = 0; a < kFA; ++a) {
             const int m = wm + 16 * a + r16;
             const i32x8 af = frag(st.a, m, g);
-            const int asc = (int)((x_scale_word(st, m) >> (8 * g)) & 0xFFu);
+            const uint32_t xw = Grouped ? scg[m * kGroupSteps] : x_scale_word(st, m);
+            const int asc = (int)((xw >> (8 * g)) & 0xFFu);
 #pragma unroll
             for (int b = 0; b < kFB; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -213,7 +256,11 @@ hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int6
     const int64_t tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
     a.tiles_m = (int32_t)tm;
     a.tiles_n = (int32_t)tn;
-    return launch1(k_mm_mx, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
+    const bool grouped = K % (kTK * kGroupSteps) == 0 && reinterpret_cast<uintptr_t>(xe) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(we) % 16 == 0 && ldxe % 16 == 0 && ldwe % 16 == 0;
+    if (grouped)
+        return launch1(k_mm_mx<true>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
+    return launch1(k_mm_mx<false>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
 }
 
 }  // namespace bq

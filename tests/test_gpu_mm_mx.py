@@ -113,13 +113,16 @@ def test_mm_mx_exact_small_integers(M, N, K):
     assert np.array_equal(y, want)
 
 
-@pytest.mark.parametrize("M,N,K", [(130, 272, 384), (257, 129, 640)])
-def test_mm_mx_padded_strides_match_dense(M, N, K):
+@pytest.mark.parametrize("M,N,K,pad_xe,pad_we", [(130, 272, 384, 12, 4), (257, 129, 640, 12, 4),
+                                                 (130, 272, 1024, 16, 32), (257, 129, 2048, 12, 4)])
+def test_mm_mx_padded_strides_match_dense(M, N, K, pad_xe, pad_we):
     """Every leading dimension padded: values by multiples of 16 bytes, scales by multiples
     of 4, the output by an odd count.  The value padding holds the E4M3 NaN code and the
     scale padding the E8M0 NaN byte, so a read past a row's K columns would show.  The
-    result equals the dense-stride launch bit for bit, and the output padding is untouched."""
-    say(f"mm_mx padded strides {M}x{N}x{K}")
+    result equals the dense-stride launch bit for bit, and the output padding is untouched.
+    K = 1024 with 16-byte scale strides takes the grouped scale loads (4 K steps per load);
+    K = 2048 with 4-byte ones falls back to per-step scales; both equal the dense launch."""
+    say(f"mm_mx padded strides {M}x{N}x{K} scale pads ({pad_xe},{pad_we})")
     x = workloads.rows(4, 3, 0, M, K)
     w = workloads.rows(6, 4, 0, N, K)
     xv, xe = oracle.quant_mx(x)
@@ -132,8 +135,8 @@ def test_mm_mx_padded_strides_match_dense(M, N, K):
         return buf[:, :a.shape[1]]
 
     xvp, wvp = padded(xv, 256, 0x7F), padded(wv, 48, 0xFF)
-    xep, wep = padded(xe, 12, 0xFF), padded(we, 4, 0xFF)
-    assert xvp.stride(0) == K + 256 and wep.stride(0) == K // 32 + 4
+    xep, wep = padded(xe, pad_xe, 0xFF), padded(we, pad_we, 0xFF)
+    assert xvp.stride(0) == K + 256 and wep.stride(0) == K // 32 + pad_we
     y = filled((M, N + 13), np.uint16, 0x5A)
     bq.bq_mm_mx(xvp, xep, wvp, wep, y[:, :N], M=M, N=N, K=K)
     sync()
