@@ -314,7 +314,27 @@ def receipt(torch, bq) -> dict:
     uuid = getattr(props, "uuid", None)
     if uuid is not None:
         out["uuid"] = str(uuid)
+    out["clocks"] = gpu_clock_levels(props)
+    # the device code measured (the .hip sources and their headers, comments left out)
+    out["source_digest"] = kernel_source_digest()
     return out
+
+
+def gpu_clock_levels(props) -> dict | None:
+    """The device's shader and memory clock levels as sysfs lists them (the level in use when
+    read is marked with *), or None where they cannot be read."""
+    try:
+        bdf = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    except (AttributeError, TypeError, ValueError):
+        return None
+    out = {}
+    for key in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        try:
+            with open(f"/sys/bus/pci/devices/{bdf}/{key}") as f:
+                out[key] = [line.strip() for line in f if line.strip()]
+        except OSError:
+            pass
+    return out or None
 
 
 def cpu_model() -> str | None:

@@ -53,6 +53,9 @@ def test_bench_line_fields():
     for k, v in d["kernels"].items():
         assert len(v["samples_us"]) == 5, k
         assert abs(statistics.median(v["samples_us"]) - v["us_per_launch"]) <= 0.011, k
-    for k in ("torch", "hip", "library", "device", "arch", "compute_units", "memory_gib"):
+    for k in ("torch", "hip", "library", "device", "arch", "compute_units", "memory_gib", "clocks",
+              "source_digest"):
         assert k in d["receipt"], k
+    import bench
+    assert d["receipt"]["source_digest"] == bench.kernel_source_digest()
     assert "gfx950" in d["receipt"]["arch"]
