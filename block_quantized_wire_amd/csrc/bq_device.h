@@ -181,12 +181,16 @@ __device__ __forceinline__ float e4m3_block_scale(float amax) {
 // round-half-even(fl32(x / s)) never exceeds 127 in magnitude -- amax / fl32(amax/127)
 // <= 127 * (1 + 2^-9) even for subnormal scales -- so the clamp to [-127, 127] of the
 // definition never changes a value and is not applied.
-// Pack the low bytes of four int-valued floats (in [-127, 127]) into one word.
-__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
-    uint32_t ia = (uint32_t)(int)a, ib = (uint32_t)(int)b;
-    uint32_t ic = (uint32_t)(int)c, id = (uint32_t)(int)d;
-    uint32_t lo = __builtin_amdgcn_perm(ib, ia, 0x0C0C0400u);   // [a0, b0, 0, 0]
-    uint32_t hi = __builtin_amdgcn_perm(id, ic, 0x04000C0Cu);   // [0, 0, c0, d0]
+// round-half-even(t) for binary32 |t| < 2^22, as a bit pattern whose low byte is the
+// result's two's-complement byte: t + 1.5 * 2^23 has ulp 1, so the binary32 sum (rounded to
+// nearest even) is exactly 1.5 * 2^23 + rint(t), bit pattern 0x4B400000 + rint(t).  Ties go
+// to even as rintf's do, and -0 and small negatives that round to zero give byte 0.
+__device__ __forceinline__ uint32_t rint_low_byte(float t) { return __float_as_uint(t + 0x1.8p23f); }
+
+// Pack the low bytes of four words into one word.
+__device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a0, b0, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);   // [0, 0, c0, d0]
     return lo | hi;
 }
 
@@ -210,11 +214,11 @@ __device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
     if (s == 0.0f)
         return u32x2{};
     const double r = recip64(s);
-    float t[8];
+    uint32_t t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        t[i] = __builtin_rintf(quot32(f[i], r));
-    return u32x2{pack_i8x4(t[0], t[1], t[2], t[3]), pack_i8x4(t[4], t[5], t[6], t[7])};
+        t[i] = rint_low_byte(quot32(f[i], r));
+    return u32x2{pack_lo_bytes(t[0], t[1], t[2], t[3]), pack_lo_bytes(t[4], t[5], t[6], t[7])};
 }
 
 // Dequantize the 8 signed payload bytes of a lane: f = fl32(q * s).  The bytes are
