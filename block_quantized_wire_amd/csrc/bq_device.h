@@ -36,7 +36,7 @@
 // v_cvt_pk_bf16_f32 rounds binary32 to bf16 to nearest even (subnormals kept, overflow
 // to infinity); v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3FN code with ties to
 // even and keeps the sign of zero, but turns magnitudes from 464 up into NaN, so its
-// inputs are first clamped to [-448, 448]; v_cvt_pk_f32_fp8 decodes exactly.
+// inputs stay below 449 in magnitude (see e4m3x4); v_cvt_pk_f32_fp8 decodes exactly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -251,13 +251,12 @@ __device__ __forceinline__ void dequant_i8x8(u32x2 w, float s, float f[8]) {
 
 // ---- OCP E4M3FN ------------------------------------------------------------------------
 
-// E4M3FN codes of four binary32 values packed into a word (a in byte 0): nearest code,
-// ties to even, magnitudes at or above 448 saturate to 448, sign of zero kept.
+// E4M3FN codes of four binary32 values of magnitude below 449 packed into a word (a in byte
+// 0): nearest code, ties to even, magnitudes above 448 saturate to 448, sign of zero kept.
+// The hardware conversion does this without a clamp below 464 (it gives NaN from there), and
+// every caller stays below 449: an MXFP8 group scale 2^e >= fl32(amax/448) leaves at most
+// 448 / (1 - 2^-24), and an E4M3-b128 quotient x / fl32(amax/448) at most 448 (1 + 2^-9).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
