@@ -221,31 +221,14 @@ __device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
     return u32x2{pack_lo_bytes(t[0], t[1], t[2], t[3]), pack_lo_bytes(t[4], t[5], t[6], t[7])};
 }
 
-// Dequantize the 8 signed payload bytes of a lane: f = fl32(q * s).  The bytes are
-// biased to unsigned (q + 128 = byte ^ 0x80) and converted exactly; a fused
-// multiply-add of u * s - 128 * s then rounds the exact product q * s once, which is
-// the binary32 product of the definition, sign of zero included when s > 0 (a zero
-// product then means q = 0, and u * s - 128 * s = +0 = 0 * s).  Other scales -- zero,
-// negative, or s >= 2^120 where 128 * s would overflow -- take the plain
-// convert-and-multiply form.
+// Dequantize the 8 signed payload bytes of a lane: f = fl32(q * s), the binary32 product of
+// the definition, for every scale.  Each byte converts exactly (one sign-extending byte
+// conversion), and one multiply rounds the product.
 __device__ __forceinline__ void dequant_i8x8(u32x2 w, float s, float f[8]) {
-    if (__builtin_expect(s > 0.0f && s < 0x1.0p120f, 1)) {
-        const uint32_t a = w.x ^ 0x80808080u, b = w.y ^ 0x80808080u;
-        const float c = -128.0f * s;
-        f[0] = __builtin_fmaf((float)(a & 0xFFu), s, c);
-        f[1] = __builtin_fmaf((float)((a >> 8) & 0xFFu), s, c);
-        f[2] = __builtin_fmaf((float)((a >> 16) & 0xFFu), s, c);
-        f[3] = __builtin_fmaf((float)(a >> 24), s, c);
-        f[4] = __builtin_fmaf((float)(b & 0xFFu), s, c);
-        f[5] = __builtin_fmaf((float)((b >> 8) & 0xFFu), s, c);
-        f[6] = __builtin_fmaf((float)((b >> 16) & 0xFFu), s, c);
-        f[7] = __builtin_fmaf((float)(b >> 24), s, c);
-    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = (float)(int)(int8_t)((w.x >> (8 * i)) & 0xFFu) * s;
-            f[i + 4] = (float)(int)(int8_t)((w.y >> (8 * i)) & 0xFFu) * s;
-        }
+    for (int i = 0; i < 4; ++i) {
+        f[i] = (float)(int)(int8_t)((w.x >> (8 * i)) & 0xFFu) * s;
+        f[i + 4] = (float)(int)(int8_t)((w.y >> (8 * i)) & 0xFFu) * s;
     }
 }
 
