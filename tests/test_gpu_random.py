@@ -142,8 +142,10 @@ def test_random_mx_and_e4m3(seed):
     # below are the same as without it
     prng = np.random.default_rng(5000 + seed)
     padx, pady = 8 * int(prng.integers(0, 3)), 8 * int(prng.integers(0, 3))
+    off, extra, spare = 128 * int(prng.integers(0, 3)), 128 * int(prng.integers(0, 2)), int(prng.integers(0, 3))
     say(f"random mx seed={seed} {fmt} {rows}x{cols} pads=({padv},{pads}) ldx pad {padx} "
-        f"ldy pad {pady}; flat n={n} nsrc={nsrc}; e4m3-b128")
+        f"ldy pad {pady}; slice at column {off} of {off + cols + extra}, {spare} spare rows; "
+        f"flat n={n} nsrc={nsrc}; e4m3-b128")
     # 2-D MXFP8 with padded strides (binary16 input: magnitudes within its range).  The input
     # padding holds NaN bit patterns, so reading it would corrupt a group's scale.
     x = draw(rng, rows * cols, lo=-20, hi=14, fmt=fmt) if fmt == "f16" else draw(rng, rows * cols)
@@ -163,6 +165,19 @@ def test_random_mx_and_e4m3(seed):
     y = host(ybuf, np.uint16)
     assert_same(y[:, :cols], oracle.dequant_mx(wv, we), "MX bf16")
     assert np.all(y[:, cols:] == 0xA5A5), "dequantize wrote into the row padding"
+    # the same padded input staged as a slice at a 128-column offset of a wider buffer with
+    # spare rows: equal to the one-call quantization, every other column and row untouched
+    total, cap = off + cols + extra, rows + spare
+    sv, se = filled((cap, total), np.uint8, 0x5A), filled((cap, total // 32), np.uint8, 0x5A)
+    stage = bq.bq_quant_mx_slice_f16 if fmt == "f16" else bq.bq_quant_mx_slice
+    stage(xbuf[:, :cols], off, sv, se, capacity_rows=cap, rows=rows, cols=cols, ldx=cols + padx)
+    sync()
+    hv, he = host(sv, np.uint8), host(se, np.uint8)
+    assert_same(hv[:rows, off:off + cols], wv, "staged slice values")
+    assert_same(he[:rows, off // 32:(off + cols) // 32], we, "staged slice scales")
+    hv[:rows, off:off + cols] = 0x5A
+    he[:rows, off // 32:(off + cols) // 32] = 0x5A
+    assert np.all(hv == 0x5A) and np.all(he == 0x5A), "the slice wrote outside its columns or rows"
     # flat MXFP8: hop in place, accumulate
     xf = draw(rng, n, hi=80)
     fv, fe = oracle.quant_mx_flat(xf)
