@@ -317,3 +317,62 @@ def test_mm_mx_errors():
     assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, y + 1, N, S) == ALIGN
     assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, xv + 256, N, S) == ALIAS
     assert f(xv, K, xe, 8, wv, K, we, 8, M, N, K, we + 16, N, S) == ALIAS
+
+
+def test_every_entry_point_accepts_empty_input():
+    # n == 0 (rows == 0, M == 0 ...) is valid for every call and launches nothing (without a
+    # GPU a launch would fail with BQ_ERR_LAUNCH, so OK shows none was tried); counts
+    # and shapes are still validated first.
+    p, q, e, y = A, A + 8192, A + 16384, A + 24576
+    one = arr(p)
+    two = arr(p, q)
+    calls = {
+        "bq_quant_i8": lambda: L.bq_quant_i8(p, 0, q, e, S),
+        "bq_dequant_i8": lambda: L.bq_dequant_i8(q, e, 0, y, S),
+        "bq_dequant_accum_i8": lambda: L.bq_dequant_accum_i8(2, two, two, 0, y, S),
+        "bq_dequant_accum_i8_batch": lambda: L.bq_dequant_accum_i8_batch(3, 2, two, two, 0, y, S),
+        "bq_a2a_reduce_i8": lambda: L.bq_a2a_reduce_i8(2, 2, two, two, 0, q, e, two, y, S),
+        "bq_ring_hop_i8": lambda: L.bq_ring_hop_i8(q, e, p, 0, q, e, S),
+        "bq_quant_i8_batch": lambda: L.bq_quant_i8_batch(1, one, 0, one, one, S),
+        "bq_dequant_i8_batch": lambda: L.bq_dequant_i8_batch(1, one, one, 0, one, S),
+        "bq_ring_hop_i8_batch": lambda: L.bq_ring_hop_i8_batch(1, one, one, one, 0, one, one, S),
+        "bq_allgather_dequant_i8": lambda: L.bq_allgather_dequant_i8(3, q, e, 0, two, 1, S),
+        "bq_ring_allreduce_i8": lambda: L.bq_ring_allreduce_i8(3, 0, two, q, e, two, S),
+        "bq_a2a_allreduce_i8": lambda: L.bq_a2a_allreduce_i8(3, 0, two, two, two, y, q, e, two,
+                                                             S),
+        "bq_quant_mx": lambda: L.bq_quant_mx(p, 0, 256, 256, q, 256, e, 8, S),
+        "bq_dequant_mx": lambda: L.bq_dequant_mx(q, 256, e, 8, 0, 256, y, 256, S),
+        "bq_quant_mx_slice": lambda: L.bq_quant_mx_slice(p, 0, 128, 128, 128, q, 256, e, 8, 0,
+                                                         S),
+        "bq_quant_mx_f16": lambda: L.bq_quant_mx_f16(p, 5, 0, 0, q, 0, e, 0, S),
+        "bq_quant_mx_slice_f16": lambda: L.bq_quant_mx_slice_f16(p, 0, 128, 128, 0, q, 128, e,
+                                                                 4, 0, S),
+        "bq_quant_mx_batch": lambda: L.bq_quant_mx_batch(1, one, 0, one, one, S),
+        "bq_dequant_mx_batch": lambda: L.bq_dequant_mx_batch(1, one, one, 0, one, S),
+        "bq_ring_hop_mx": lambda: L.bq_ring_hop_mx(q, e, p, 0, q, e, S),
+        "bq_ring_hop_mx_batch": lambda: L.bq_ring_hop_mx_batch(1, one, one, one, 0, one, one, S),
+        "bq_dequant_accum_mx": lambda: L.bq_dequant_accum_mx(2, two, two, 0, y, S),
+        "bq_a2a_reduce_mx": lambda: L.bq_a2a_reduce_mx(2, 2, two, two, 0, q, e, None, None, S),
+        "bq_allgather_dequant_mx": lambda: L.bq_allgather_dequant_mx(3, q, e, 0, two, 0, S),
+        "bq_ring_allreduce_mx": lambda: L.bq_ring_allreduce_mx(3, 0, two, q, e, two, S),
+        "bq_a2a_allreduce_mx": lambda: L.bq_a2a_allreduce_mx(3, 0, two, two, two, None, q, e,
+                                                             two, S),
+        "bq_mm_mx": lambda: L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 0, 64, 256, y, 64, S),
+        "bq_quant_e4m3_b128": lambda: L.bq_quant_e4m3_b128(p, 0, q, e, S),
+        "bq_dequant_e4m3_b128": lambda: L.bq_dequant_e4m3_b128(q, e, 0, y, S),
+    }
+    compute = [n for n in declared_symbols()
+               if n not in ("bq_status_str", "bq_version", "bq_wire_bytes_b128",
+                            "bq_mx_staging_bytes")]
+    assert sorted(calls) == compute
+    for name, call in calls.items():
+        assert call() == OK, name
+    # N == 0 is empty too; K is not a size that may be zero
+    assert L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 64, 0, 256, y, 64, S) == OK
+    assert L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 0, 0, 0, y, 64, S) == SIZE
+    # an empty call still rejects a bad count or a size off its block
+    assert L.bq_quant_i8_batch(0, one, 0, one, one, S) == NSRC
+    assert L.bq_dequant_accum_i8(0, two, two, 0, y, S) == NSRC
+    assert L.bq_ring_allreduce_i8(17, 0, two, q, e, two, S) == NSRC   # 16 ranks at most
+    assert L.bq_quant_mx(p, 0, 100, 128, q, 128, e, 4, S) == SIZE
+    assert L.bq_quant_mx_slice(p, 1, 128, 128, 128, q, 256, e, 8, 0, S) == BOUNDS
