@@ -113,6 +113,25 @@ MUTANTS = [
     ("A2A requantizes only the first shard", "for (int j = 0; j < W; j++) {\n        for (int s = 0; s < W; s++) {",
      "for (int j = 0; j < 1; j++) {\n        for (int s = 0; s < W; s++) {",
      ["test_a2a_requantizes_the_bf16_sum"]),
+    ("staged slice scales at column off/128",
+     "orc_quant_mx(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / MXG, lds);",
+     "orc_quant_mx(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / 128, lds);",
+     ["test_mx_slices_equal_concatenation_and_leave_the_rest_untouched"]),
+    ("binary16 staged slice values at column off/2",
+     "orc_quant_mx_f16(x, rows, cols, ldx, v + col_off, ldv, e8m0 + col_off / MXG, lds);",
+     "orc_quant_mx_f16(x, rows, cols, ldx, v + col_off / 2, ldv, e8m0 + col_off / MXG, lds);",
+     ["test_mx_f16_slices_equal_concatenation_and_leave_the_rest_untouched"]),
+    ("MX dequant reads the scale of column c/128", "e8m0[r * lds + c / MXG]",
+     "e8m0[r * lds + c / 128]", ["test_mx_dequant_matches_torch_decode"]),
+    ("binary16 rows decoded as bf16", "quant_mx_rows(orc_f16_to_f32, x",
+     "quant_mx_rows(orc_bf16_to_f32, x", ["test_mx_f16_quant_bruteforce_rows"]),
+    ("E4M3 subnormal step 2^-10", "mag = ldexpf((float)man, -9);", "mag = ldexpf((float)man, -10);",
+     ["test_e4m3_decode_all_codes"]),
+    ("E4M3-b128 dequant uses the first block's scale",
+     "float val = orc_e4m3_decode(v[i]) * scale[i / BLK];",
+     "float val = orc_e4m3_decode(v[i]) * scale[0];", ["test_e4m3_b128_bruteforce_and_dequant"]),
+    ("E4M3 saturates to the NaN code", "return (uint8_t)(sign | 0x7E);",
+     "return (uint8_t)(sign | 0x7F);", ["test_e4m3_encode_signed_zero_and_saturation"]),
 ]
 
 
