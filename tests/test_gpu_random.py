@@ -7,8 +7,14 @@ all-zero blocks.  Every output is compared bit for bit with the oracle, whose in
 the same host arrays (payloads for a hop or an accumulate are the oracle's own
 quantization of drawn tensors, never the GPU's).  The case about to run is printed
 first, so a failure names its seed and shape.
+
+BQ_RANDOM_CASES (default 24) sets the number of seeds per codec family, and a twelfth of it
+(at least 12) the number of GEMM shapes; the default seeds are the first ones of any
+longer sweep.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -24,7 +30,8 @@ import block_quantized_wire_amd as bq  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = int(os.environ.get("BQ_RANDOM_CASES", "24"))
+MM_CASES = max(12, CASES // 12)
 
 
 def assert_same(got, want, what):
@@ -207,7 +214,7 @@ def test_random_mx_and_e4m3(seed):
     assert_same(host(ye, np.uint16), oracle.dequant_e4m3_b128(wev, wes), "E4M3-b128 bf16")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(MM_CASES))
 def test_random_mm_mx(seed):
     """Random GEMM shapes (ragged M and N, K up to 2048): operands are the oracle's MXFP8
     quantization of drawn values, within the bound derived from the matrix cores'
