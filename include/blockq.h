@@ -15,7 +15,9 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.  INT8 payloads are int8_t, E4M3
  *     and E8M0 bytes are uint8_t, per-block scales are float (IEEE binary32).
  *   - n counts values; it must be a multiple of 128 (a block, P1 Summary; the per-rank
- *     shard rule of P2 Configuration).  n == 0 is valid and launches nothing.
+ *     shard rule of P2 Configuration).  n == 0 is valid and launches nothing, as are
+ *     rows == 0 or cols == 0 (MXFP8) and M == 0 or N == 0 (GEMM); the counts and the other
+ *     sizes are still validated first, and no pointer is read.
  *     Limits: n / 128 < 2^36 (else BQ_ERR_SIZE); a row-major operand of rows x cols with
  *     row stride ld spans at most 2^48 bytes, ((rows - 1) * ld + cols) * element size
  *     (else BQ_ERR_BOUNDS); the MXFP8 calls take rows * cols / 128 < 2^31 blocks, and

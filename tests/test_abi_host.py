@@ -367,6 +367,12 @@ def test_every_entry_point_accepts_empty_input():
     assert sorted(calls) == compute
     for name, call in calls.items():
         assert call() == OK, name
+    # an empty call reads no pointer, so NULL ones are accepted too
+    assert L.bq_quant_i8(None, 0, None, None, S) == OK
+    assert L.bq_ring_allreduce_i8(3, 0, None, None, None, None, S) == OK
+    assert L.bq_a2a_allreduce_mx(3, 0, None, None, None, None, None, None, None, S) == OK
+    assert L.bq_quant_mx_slice(None, 0, 128, 128, 0, None, 128, None, 4, 0, S) == OK
+    assert L.bq_mm_mx(None, 256, None, 8, None, 256, None, 8, 0, 64, 256, None, 64, S) == OK
     # N == 0 is empty too; K is not a size that may be zero
     assert L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 64, 0, 256, y, 64, S) == OK
     assert L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 0, 0, 0, y, 64, S) == SIZE
