@@ -59,10 +59,11 @@ def bf16_bits_to_fraction(h: int) -> Fraction:
 
 
 def fraction_to_bf16_bits(v: Fraction) -> int:
-    """bf16 bit pattern of the bf16 rounding of v (v must round to a finite value; zero -> +0)."""
+    """bf16 bit pattern of the bf16 rounding of v (v must round to a finite value).  Zero
+    gives +0; a negative v that rounds to zero gives -0, as IEEE rounding keeps the sign."""
     r = round_binary(v, BF16)
     if r == 0:
-        return 0
+        return 0x8000 if v < 0 else 0
     sign = 0x8000 if r < 0 else 0
     a = abs(r)
     e = a.numerator.bit_length() - a.denominator.bit_length()
@@ -75,11 +76,13 @@ def fraction_to_bf16_bits(v: Fraction) -> int:
 
 
 def nearest_int_even(t: Fraction, lo: int, hi: int) -> int:
-    """argmin over k in [lo, hi] of |t - k|, ties to the even k."""
+    """argmin over k in [lo, hi] of |t - k|, ties to the even k.  With t = N/D (D > 0) the
+    distances are compared as the integers |N - kD|, which orders them the same way."""
+    t = Fraction(t)
+    num, den = t.numerator, t.denominator
     best = None
     for k in range(lo, hi + 1):
-        d = abs(t - k)
-        key = (d, k % 2)
+        key = (abs(num - k * den), k % 2)
         if best is None or key < best[0]:
             best = (key, k)
     return best[1]

@@ -130,6 +130,11 @@ MUTANTS = [
     ("E4M3-b128 dequant uses the first block's scale",
      "float val = orc_e4m3_decode(v[i]) * scale[i / BLK];",
      "float val = orc_e4m3_decode(v[i]) * scale[0];", ["test_e4m3_b128_bruteforce_and_dequant"]),
+    ("INT8 quotients not clamped to [-127, 127]",
+     "        if (r > I8_QMAX)\n            r = I8_QMAX;\n        if (r < -I8_QMAX)\n            r = -I8_QMAX;\n",
+     "",
+     ["test_ring_hop_clamps_the_quotients_of_few_bit_subnormal_scales",
+      "test_ring_allreduce_of_cancelling_partials_clamps_like_the_brute_force"]),
     ("E4M3 saturates to the NaN code", "return (uint8_t)(sign | 0x7E);",
      "return (uint8_t)(sign | 0x7F);", ["test_e4m3_encode_signed_zero_and_saturation"]),
 ]

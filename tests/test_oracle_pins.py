@@ -341,6 +341,90 @@ def test_ring_hop_scale_underflow_is_a_zero_block():
     assert bf.rn32(Fraction(2) ** -149 / 127) == 0  # the scale really underflows
 
 
+def test_ring_hop_clamps_the_quotients_of_few_bit_subnormal_scales():
+    """A hop requantizes binary32 sums, whose block amax can be A * 2^-149 for a small
+    integer A.  Its scale fl32(amax/127) is then a subnormal with only a few significant
+    bits, so x/scale can exceed 127.5: A = 190 gives scale 2^-149 and quotient 190.  The
+    block-INT8 range [-127, 127] clamps such quotients.  Every A in 128..16065 against the
+    exact-rational brute force: payload [1, -1, 0, ...] with input scale A * 2^-149 and a
+    zero local partial, so the sums are +-A * 2^-149 and zeros."""
+    As = np.arange(128, 16066)
+    nb = As.size
+    q = np.zeros((nb, 128), np.int8)
+    q[:, 0], q[:, 1] = 1, -1
+    s = (As.astype(np.float64) * 2.0 ** -149).astype(np.float32)
+    q2, s2 = oracle.ring_hop_i8(q.reshape(-1), s, np.zeros(nb * 128, np.uint16))
+    q2 = q2.reshape(nb, 128)
+    assert not q2[:, 2:].any()
+    binding = 0
+    for b, A in enumerate(As.tolist()):
+        assert Fraction(float(s[b])) == A * Fraction(2) ** -149         # input scale exact
+        wq, ws = bf.hop_block([1, -1, 0], A * Fraction(2) ** -149, [0, 0, 0])
+        assert Fraction(float(s2[b])) == ws
+        assert [int(q2[b, 0]), int(q2[b, 1]), 0] == wq, A
+        binding += bf.rn32(A * Fraction(2) ** -149 / ws) > Fraction(255, 2)
+    assert binding > 3000          # the clamp decides thousands of these blocks
+    # the two cases worked by hand: scale 2^-149 with quotient 190, and scale 39 * 2^-149
+    # with quotient 5000/39 = 128.2; both clamp to +-127
+    for A, scale_units in ((190, 1), (5000, 39)):
+        b = A - 128
+        assert Fraction(float(s2[b])) == scale_units * Fraction(2) ** -149
+        assert (int(q2[b, 0]), int(q2[b, 1])) == (127, -127)
+
+
+def test_ring_allreduce_of_cancelling_partials_clamps_like_the_brute_force():
+    """A W = 2 ring whose bf16 partials nearly cancel reaches the clamp through the public
+    schedule.  The quantizing rank's block holds the pilot 2^-126 (q = 127 under the scale
+    fl32(2^-126/127) = 66052 * 2^-149) and values k * 2^-133 with |k| <= K (q = k); the
+    hopping rank holds minus the bf16 rounding of each dequantized value.  The hop sums are
+    then -4 * 2^-149 at the pilot and 516 k * 2^-149 elsewhere, so the block amax is
+    516 K * 2^-149 and for K <= 7 its scale 4 K * 2^-149 leaves the quotient 129, clamped to
+    127.  The final payload and both ranks' outputs are checked against the exact-rational
+    brute force of the schedule (chunk c quantized by rank c+1, hopped by rank c)."""
+    W, nbc = 2, 9
+    m = nbc * 128
+    rng = np.random.default_rng(12)
+    two = Fraction(2)
+    quant_side = np.zeros((W, m), np.uint16)     # partial of the rank that quantizes chunk c
+    hop_side = np.zeros((W, m), np.uint16)       # partial of the rank that hops chunk c
+    for c in range(W):
+        for b in range(nbc):
+            K = b + 1 if b < 7 else (31 if b == 7 else 63)
+            k = rng.integers(-K, K + 1, 128)
+            k[0], k[1 + c], k[5] = 0, K, -K
+            vals = [Fraction(int(v)) * two ** -133 for v in k]
+            vals[0] = two ** -126
+            blk = slice(b * 128, (b + 1) * 128)
+            quant_side[c, blk] = [bf.fraction_to_bf16_bits(v) for v in vals]
+            wq, ws = bf.quant_i8_block(vals)
+            assert ws == 66052 * two ** -149 and wq[0] == 127 and wq[1:] == [int(v) for v in k[1:]]
+            hop_side[c, blk] = [bf.fraction_to_bf16_bits(-bf.rn32(qv * ws)) for qv in wq]
+    # rank r quantizes chunk (r - 1) mod W and hops chunk r
+    partials = [np.zeros(W * m, np.uint16) for _ in range(W)]
+    for c in range(W):
+        partials[(c + 1) % W][c * m:(c + 1) * m] = quant_side[c]
+        partials[c][c * m:(c + 1) * m] = hop_side[c]
+    q_fin, s_fin, outs = oracle.ring_allreduce_i8(partials)
+    clamped = 0
+    for c in range(W):
+        for b in range(nbc):
+            blk = slice(b * 128, (b + 1) * 128)
+            xs = [bf.bf16_bits_to_fraction(int(h)) for h in quant_side[c, blk]]
+            q1, s1 = bf.quant_i8_block(xs)
+            wq, ws = bf.hop_block(q1, s1, [int(h) for h in hop_side[c, blk]])
+            off = c * m + b * 128
+            assert Fraction(float(s_fin[off // 128])) == ws
+            assert q_fin[off:off + 128].tolist() == wq
+            want = [bf.dequant_i8_value(qv, ws) for qv in wq]
+            for r in range(W):
+                assert outs[r][off:off + 128].tolist() == want
+            amax = 516 * (b + 1 if b < 7 else (31 if b == 7 else 63)) * two ** -149
+            if bf.rn32(amax / ws) > Fraction(255, 2):
+                clamped += 1
+                assert wq[1 + c] == 127 and wq[5] == -127
+    assert clamped == 2 * 7
+
+
 def _chain_position(r: int, c: int, W: int) -> int:
     return (r - c - 1) % W
 
