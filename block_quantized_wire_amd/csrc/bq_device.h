@@ -177,10 +177,6 @@ __device__ __forceinline__ float e4m3_block_scale(float amax) {
     return (float)((double)amax * (1.0 / 448.0));
 }
 
-// Quotient rounding of the block-INT8 rule for |x| <= amax, s = fl32(amax/127):
-// round-half-even(fl32(x / s)) never exceeds 127 in magnitude -- amax / fl32(amax/127)
-// <= 127 * (1 + 2^-9) even for subnormal scales -- so the clamp to [-127, 127] of the
-// definition never changes a value and is not applied.
 // round-half-even(t) for binary32 |t| < 2^22, as a bit pattern whose low byte is the
 // result's two's-complement byte: t + 1.5 * 2^23 has ulp 1, so the binary32 sum (rounded to
 // nearest even) is exactly 1.5 * 2^23 + rint(t), bit pattern 0x4B400000 + rint(t).  Ties go
@@ -207,18 +203,35 @@ __device__ __forceinline__ double recip64(float s) {
 // fl32(x / s) exactly (see the header comment), given r = recip64(s).
 __device__ __forceinline__ float quot32(float x, double r) { return (float)((double)x * r); }
 
-// Quantize 8 binary32 values of one lane with its block's scale.  A block whose
-// amax is 0 -- or whose scale underflows to 0, which only binary32 sums can reach --
-// is a zero block: scale 0, payload 0.
+// Quantize 8 binary32 values of one lane with its block's scale s = fl32(amax/127):
+// q = round-half-even(fl32(x/s)) clamped to [-127, 127].  A block whose amax is 0 -- or
+// whose scale underflows to 0, which only binary32 sums can reach -- is a zero block:
+// scale 0, payload 0.
+// The clamp can only bind when s is subnormal.  A normal s is within 2^-24 (relative) of
+// amax/127, so |x/s| <= 127 (1 + 2^-23) rounds to at most 127.  A subnormal s keeps only
+// the bits above 2^-149, and with few of them the quotient overshoots: amax = 190 * 2^-149
+// (a ring hop's binary32 sums reach such values) gives s = 2^-149 and x/s = 190.  Below
+// the normal range amax < 127 * 2^-126 and |x/s| <= 190 < 2^22, so rint_low_byte's range
+// holds before the clamp too.  Blocks with a subnormal scale are rare, so the clamp sits
+// behind a branch that waves skip when none of their lanes has one.
 __device__ __forceinline__ u32x2 quant_i8x8(const float f[8], float s) {
     if (s == 0.0f)
         return u32x2{};
     const double r = recip64(s);
-    uint32_t t[8];
+    float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        t[i] = rint_low_byte(quot32(f[i], r));
-    return u32x2{pack_lo_bytes(t[0], t[1], t[2], t[3]), pack_lo_bytes(t[4], t[5], t[6], t[7])};
+        t[i] = quot32(f[i], r);
+    if (s < 0x1p-126f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = __builtin_fminf(__builtin_fmaxf(t[i], -127.0f), 127.0f);
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        b[i] = rint_low_byte(t[i]);
+    return u32x2{pack_lo_bytes(b[0], b[1], b[2], b[3]), pack_lo_bytes(b[4], b[5], b[6], b[7])};
 }
 
 // Dequantize the 8 signed payload bytes of a lane: f = fl32(q * s), the binary32 product of

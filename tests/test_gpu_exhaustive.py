@@ -4,9 +4,10 @@ Every block holds one amax value A (each positive finite bf16, alternating sign)
 bf16 values x with |x| <= A.  Over all blocks, every pair (x, A) with |x| <= A -- both
 signs and both zeros -- occurs exactly once: about 1.07e9 values.  Payloads, scales
 and materialized bf16 outputs are compared bit for bit with the oracle, chunk by chunk.
-This covers the kernel's branch-free quotient (fl32 of x times an fp64 reciprocal of
-the scale refined by two Newton steps, exact by a midpoint-distance argument) and its
-FMA dequantize on every input the codec can receive from bf16 data.
+This covers the kernel's quotient (fl32 of x times an fp64 reciprocal of the scale
+refined by two Newton steps, exact by a midpoint-distance argument) and its dequantize
+(one binary32 product of the payload byte and the scale) on every input the codec can
+receive from bf16 data.
 """
 from __future__ import annotations
 

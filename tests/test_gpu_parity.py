@@ -205,6 +205,90 @@ def test_ring_hop_scale_underflow_zero_block():
     assert ws[0] == 0
 
 
+def test_ring_hop_clamps_few_bit_subnormal_scales():
+    """Hop blocks whose binary32 sums have amax A * 2^-149 for every A in 1..2^20: the scale
+    fl32(amax/127) is subnormal with few significant bits, the quotient can exceed 127.5
+    (A = 190: scale 2^-149, quotient 190) and the [-127, 127] clamp decides the byte.
+    Payload [1, -1, 0, ...] with input scale A * 2^-149 and a zero local partial; out of
+    place and in place, bit for bit."""
+    say("ring hop clamp: amax A*2^-149, A = 1..2^20")
+    A = np.arange(1, 2 ** 20 + 1, dtype=np.float64)
+    nb = A.size
+    n = nb * 128
+    q = np.zeros((nb, 128), np.int8)
+    q[:, 0], q[:, 1] = 1, -1
+    q = q.reshape(-1)
+    s = (A * 2.0 ** -149).astype(np.float32)
+    assert np.array_equal(s.astype(np.float64) * 2.0 ** 149, A)
+    loc = np.zeros(n, np.uint16)
+    wq, ws = oracle.ring_hop_i8(q, s, loc)
+    # the clamp binds on thousands of these blocks
+    nz = ws > 0
+    assert np.count_nonzero(s[nz].astype(np.float64) / ws[nz] > 127.5) > 4000
+    qi, si, ld = to_dev(q), to_dev(s), to_dev(loc)
+    qo, so = empty(n, np.int8), empty(nb, np.float32)
+    bq.bq_ring_hop_i8(qi, si, ld, qo, so, n=n)
+    sync()
+    assert_same(host(qo, np.int8), wq, "hop payload")
+    assert_same(host(so, np.float32), ws, "hop scales")
+    bq.bq_ring_hop_i8(qi, si, ld, qi, si, n=n)
+    sync()
+    assert_same(host(qi, np.int8), wq, "in-place hop payload")
+    assert_same(host(si, np.float32), ws, "in-place hop scales")
+
+
+def _cancelling_ring_partials(W: int, blocks: int, seed: int):
+    """Partials of a W-rank ring whose hop sums nearly cancel near 2^-126.  The rank that
+    quantizes chunk c at step 0 holds, per block, a pilot (128 + j) * 2^-133 (a bf16 normal
+    just above 2^-126) and values k * 2^-133 with |k| <= K; the next rank holds minus the
+    bf16 materialization of that payload (from the oracle), every later rank zeros.  The
+    first hop's binary32 sums are then the few-bit residues of the scale's rounding."""
+    rng = np.random.default_rng(seed)
+    m = blocks * 128
+    n = W * m
+    parts = [np.zeros(n, np.uint16) for _ in range(W)]
+    for c in range(W):
+        K = np.where(rng.random(blocks) < 0.5, rng.integers(1, 8, blocks),
+                     rng.integers(1, 64, blocks))
+        k = rng.integers(-63, 64, (blocks, 128))
+        k = np.clip(k, -K[:, None], K[:, None])
+        k[:, 1], k[:, 2] = K, -K
+        mag = np.abs(k).astype(np.uint32)
+        bits = np.where(k < 0, 0x8000, 0).astype(np.uint32) | mag   # k * 2^-133: bf16 subnormal
+        pilot = (128 + rng.integers(0, 128, blocks)).astype(np.uint32)   # (128+j) * 2^-133
+        bits[:, 0] = (1 << 7) | (pilot - 128)                           # exponent field 1
+        quant_side = bits.astype(np.uint16).reshape(-1)
+        qq, ss = oracle.quant_i8(quant_side)
+        hop_side = oracle.dequant_i8(qq, ss) ^ np.uint16(0x8000)
+        parts[(c + 1) % W][c * m:(c + 1) * m] = quant_side
+        parts[(c + 2) % W][c * m:(c + 1) * m] = hop_side
+    return parts
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_ring_allreduce_cancelling_partials(W):
+    """The clamp reached through the public ring driver: partials that cancel to few-bit
+    binary32 residues at the first hop, compared bit for bit with the oracle (final
+    payload, scales, every rank's output)."""
+    say(f"ring allreduce W={W}, cancelling partials near 2^-126")
+    blocks = 4096
+    parts = _cancelling_ring_partials(W, blocks, 40 + W)
+    # the first hop of chunk 0 reaches the clamp on many blocks
+    m = blocks * 128
+    q1, s1 = oracle.quant_i8(parts[1 % W][:m])
+    sums = (q1.astype(np.float64).reshape(-1, 128) * s1.astype(np.float64)[:, None]
+            + f32(parts[2 % W][:m]).astype(np.float64).reshape(-1, 128))
+    _, s2 = oracle.ring_hop_i8(q1, s1, parts[2 % W][:m])
+    nz = s2 > 0
+    assert np.count_nonzero(np.abs(sums).max(1)[nz] / s2[nz] > 127.5) > 100
+    wq, ws, wouts = oracle.ring_allreduce_i8(parts)
+    _, qw, sw, outs = gpu_ring(parts)
+    assert_same(host(qw, np.int8), wq, "final payloads")
+    assert_same(host(sw, np.float32), ws, "final scales")
+    for r in range(W):
+        assert_same(host(outs[r], np.uint16), wouts[r], f"rank {r} output")
+
+
 def gpu_ring(partials: list[np.ndarray]):
     W, n = len(partials), partials[0].size
     pd = [to_dev(p.reshape(-1)) for p in partials]
