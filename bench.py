@@ -11,15 +11,26 @@ simulated ranks, each holding a 3072x7168 bf16 partial (N(0, 0.5)), go through
   * MXFP8: the four partials staged as 128-aligned slices of a 3072x28672 buffer,
     then dequantized;
   * the E4M3 128-block codec on rank 0's partial, quantize and dequantize.
-`value` is the algorithmic bytes of the step (each kernel's inputs read once and
-outputs written once; the four ranks' materialization reads its one shared payload
-once) over the step time, in GB/s; HBM peak is 8 TB/s.  Inputs are resident in HBM.
-Four complete buffer sets (inputs, intermediates, outputs; about 1 GB each) rotate
-step by step, so a step's inputs are cold in the 256 MB last-level cache while what
-a kernel consumes from the previous kernel of the same step may be served by it, as
-in any pipeline on one GPU.
+
+`value` is the metric itself: the block-INT8 quantize of the ring's step-0 chunks
+(4 ranks x 768x7168, 3072x7168 values in one launch) followed by the three 4-rank
+fused ring-hop steps, timed as a region of its own (K passes back to back), as
+algorithmic bytes (each kernel's inputs read once, outputs written once) over time,
+in GB/s against the 8 TB/s HBM peak.  The whole step is reported beside it
+(`step`), and so is every distinct kernel of the step alone (`kernels`), each of
+the five workload configurations at full size (`configs`) and the staged MXFP8
+GEMM (`gemm`).  Inputs are resident in HBM.  Four complete buffer sets (inputs,
+intermediates, outputs; about 1 GB each) rotate pass by pass, so a pass's inputs
+are cold in the 256 MB last-level cache while what a kernel consumes from the
+previous kernel of the same pass may be served by it, as in any pipeline on one GPU.
+
+Every timed region starts behind a 1 GiB device copy queued on the same stream, so
+the host has enqueued the region's launches before the GPU reaches them: the events
+then bracket GPU work only, with no gap waiting for the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --sweep             (quantize, hop and copy from 8 MB to 1 GB)
+       python bench.py --summarize-trace CSV   (rocprofv3 kernel trace -> table)
 """
 from __future__ import annotations
 
@@ -45,7 +56,9 @@ N = ROWS * COLS
 NB = N // 128
 M = N // W                 # values per ring chunk / A2A shard
 SETS = 4                   # rotating buffer sets, each a full step's inputs and outputs (~1 GB)
-SAMPLES = 5                # timed samples per kernel in timed region 2 (median reported)
+SAMPLES = 5                # timed samples per region (median reported)
+REPS = 20                  # back-to-back launches per sample when a kernel is timed alone
+CONFIG_PASSES = 10         # passes per sample of each workload configuration
 
 # algorithmic bytes per 128 values of each kernel (inputs read once, outputs written once)
 B_QUANT = 256 + 132        # bf16 in; int8 + fp32 scale out
@@ -124,7 +137,7 @@ class Step:
         A = lambda ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
         P = lambda t: t.data_ptr()
         MB = M // 128
-        self.calls, self.kernels, self.next_kernels = [], [], []
+        self.calls, self.kernels, self.next_kernels, self.metric = [], [], [], []
         for b in self.sets:
             parts = b["parts"]
             calls, kern, nxt = [], [], []
@@ -211,25 +224,250 @@ class Step:
             self.calls.append(calls)
             self.kernels.append(kern)
             self.next_kernels.append(nxt)
+            # the metric: the ring's step-0 quantize and its three hop steps
+            self.metric.append(kern[:W])
         assert sum(c[1] for c in self.calls[0]) == sum(k[1] for k in self.kernels[0])
+        assert [k[0] for k in self.metric[0]] == ["quant_i8 x4"] + ["ring_hop_i8 x4"] * (W - 1)
 
     @property
     def step_bytes(self) -> int:
         return sum(c[1] for c in self.calls[0])
 
-    def run(self, i: int) -> None:
-        for name, _, fn, args in self.calls[i % len(self.calls)]:
-            st = fn(*args)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({self.bq.bq_status_str(st)})")
+    @property
+    def metric_bytes(self) -> int:
+        return sum(c[1] for c in self.metric[0])
 
-    def run_kernels(self, i: int, events) -> None:
-        for k, (name, _, fn, args) in enumerate(self.kernels[i % len(self.kernels)]):
-            events[k][0].record(self.stream)
-            st = fn(*args)
-            events[k][1].record(self.stream)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({self.bq.bq_status_str(st)})")
+    def run(self, i: int) -> None:
+        run_calls(self.calls[i % len(self.calls)])
+
+    def run_metric(self, i: int) -> None:
+        run_calls(self.metric[i % len(self.metric)])
+
+
+def run_calls(calls) -> None:
+    """Launch a list of pre-marshalled (name, bytes, C function, args) calls."""
+    for name, _, fn, args in calls:
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{name}: status {st}")
+
+
+class Region:
+    """Timing of launches on one stream between two HIP events.  A 1 GiB device copy is
+    queued first, on the same stream: it keeps the GPU busy for about 0.3 ms while the
+    host enqueues the region's launches, so the GPU never waits for the host inside the
+    region and the events bracket GPU work only.  It also evicts the 256 MB last-level
+    cache, so the region's first inputs are cold."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def time_us(self, launch) -> float:
+        """Microseconds from the first to the last of the launches `launch()` enqueues."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            self.dst.copy_(self.src)
+        e0.record(self.stream)
+        launch()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+
+def time_kernels(region: Region, seqs, reps: int, samples: int) -> dict:
+    """Each distinct kernel of `seqs` (a list, one per buffer set, of call lists) alone:
+    `reps` back-to-back launches rotating over the buffer sets (consecutive launches share
+    no buffer, so inputs are cold in the last-level cache) between one pair of events, in
+    `samples` samples taken round-robin over the kernels; the median is reported."""
+    kinds = {}
+    for k, (name, nbytes, _, _) in enumerate(seqs[0]):
+        kinds.setdefault((name, nbytes), []).append(k)
+    got = {key: [] for key in kinds}
+    for smp in range(samples):
+        for key, idx in kinds.items():
+            def launch(smp=smp, idx=idx):
+                for i in range(smp * reps, (smp + 1) * reps):
+                    run_calls([seqs[i % len(seqs)][idx[i % len(idx)]]])
+            got[key].append(region.time_us(launch) / reps)
+    out = {}
+    for (name, nbytes), idx in kinds.items():
+        us = statistics.median(got[(name, nbytes)])
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_pass": len(idx),
+                                       "us_per_launch": round(us, 2), "gbs": round(gbs, 1),
+                                       "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                       "us_per_pass": us * len(idx),
+                                       "samples_us": [round(t, 2) for t in got[(name, nbytes)]]}
+    return out
+
+
+def rate(nbytes: int, values: int, us: float) -> dict:
+    """A pass's throughput as GB/s and as values per second, each against the HBM peak
+    (the values-per-second bound is the peak over the pass's bytes per value)."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    vps = values / (us * 1e-6)
+    bound = HBM_PEAK_GBS * 1e9 / (nbytes / values)
+    return {"us_per_pass": round(us, 2), "bytes_per_pass": nbytes, "gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "values_per_pass": values,
+            "elements_per_s": round(vps, -6), "bytes_per_element": round(nbytes / values, 4),
+            "elements_frac": round(vps / bound, 4)}
+
+
+class ConfigRun:
+    """One workload configuration at full size: per buffer set, the pass as a user runs it
+    (`calls`, the public entry points) and as its kernel launches (`kernels`, for the
+    per-kernel table); `values` counts the values a pass delivers."""
+
+    def __init__(self, name, values, calls, kernels, keep):
+        self.name, self.values, self.calls, self.kernels = name, values, calls, kernels
+        self.keep = keep     # the device buffers, held while the config runs
+        self.nbytes = sum(c[1] for c in calls[0])
+        assert self.nbytes == sum(k[1] for k in kernels[0])
+
+
+def _dev_sets(torch, host_arrays, sets):
+    """`sets` device copies of each host array (bf16 bits as int16): the buffer sets hold
+    the same values at different addresses."""
+    base = [torch.from_numpy(a.reshape(-1).view(np.int16)).to("cuda") for a in host_arrays]
+    return [base] + [[t.clone() for t in base] for _ in range(sets - 1)]
+
+
+def build_configs(torch, bq, stream, which):
+    """The five workload configurations, seeded synthetic inputs at full size."""
+    import workloads
+    L = bq.lib
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    A = lambda ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
+    P = lambda t: t.data_ptr()
+    e = lambda n, dt: torch.empty(n, dtype=dt, device="cuda")
+    i16, i8, u8, f32 = torch.int16, torch.int8, torch.uint8, torch.float32
+    for cfg in which:
+        if cfg == "cfg1":
+            # block-INT8 round trip of one 512x7168 tensor; 28 buffer sets (~0.5 GB)
+            R1, n = 512, 512 * COLS
+            nb = n // 128
+            sets = 28
+            xs = _dev_sets(torch, [workloads.rows(1, 0, 0, R1, COLS)], sets)
+            calls, kern, keep = [], [], []
+            for (x,) in xs:
+                q, sc, y = e(n, i8), e(nb, f32), e(n, i16)
+                keep += [x, q, sc, y]
+                c = [("quant_i8", nb * B_QUANT, L.bq_quant_i8, (P(x), n, P(q), P(sc), sp)),
+                     ("dequant_i8", nb * B_DEQUANT, L.bq_dequant_i8, (P(q), P(sc), n, P(y), sp))]
+                calls.append(c)
+                kern.append(c)
+            yield ConfigRun("cfg1: block-INT8 quantize + dequantize round trip, 512x7168 bf16",
+                            n, calls, kern, keep)
+        elif cfg in ("cfg3_w4", "cfg3_w16"):
+            Wc = 4 if cfg == "cfg3_w4" else 16
+            n, nb = N, NB
+            m, mb = n // Wc, NB // Wc
+            host = [workloads.rows(3, r, 0, ROWS, COLS) for r in range(Wc)]
+            sets = 2
+            calls, kern, keep = [], [], []
+            for parts in _dev_sets(torch, host, sets):
+                qs = [e(n, i8) for _ in range(Wc)]
+                ss = [e(nb, f32) for _ in range(Wc)]
+                qb, sb = e(n, i8), e(nb, f32)
+                outs = [e(n, i16) for _ in range(Wc)]
+                keep += parts + qs + ss + [qb, sb] + outs
+                xa, qa, sa, oa = (A([P(t) for t in v]) for v in (parts, qs, ss, outs))
+                own = A([P(outs[j]) + 2 * m * j for j in range(Wc)])
+                b_q, b_r, b_g = Wc * nb * B_QUANT, nb * B_A2A_REDUCE(Wc), nb * B_ALLGATHER_SKIP(Wc)
+                calls.append([("i8_a2a_allreduce", b_q + b_r + b_g, L.bq_a2a_allreduce_i8,
+                               (Wc, n, xa, qa, sa, None, P(qb), P(sb), oa, sp))])
+                kern.append([(f"quant_i8 x{Wc}", b_q, L.bq_quant_i8_batch, (Wc, xa, n, qa, sa, sp)),
+                             (f"a2a_reduce_i8 {Wc}src x{Wc} owners", b_r, L.bq_a2a_reduce_i8,
+                              (Wc, Wc, qa, sa, m, P(qb), P(sb), own, None, sp)),
+                             (f"allgather_dequant_i8 x{Wc} skip own", b_g,
+                              L.bq_allgather_dequant_i8, (Wc, P(qb), P(sb), n, oa, 1, sp))])
+            yield ConfigRun(f"cfg3: i8_a2a all-reduce, {Wc} ranks x 3072x7168 bf16 "
+                            f"(shards {ROWS // Wc}x7168), 0.3*t(4)", n, calls, kern, keep)
+        elif cfg == "cfg4":
+            MR, K6 = 4096, 6
+            ldv, lds = K6 * COLS, K6 * COLS // 32
+            host = [workloads.rows(4, j, 0, MR, COLS) for j in range(K6)]
+            nb_slice = MR * COLS // 128
+            calls, kern, keep = [], [], []
+            for sl in _dev_sets(torch, host, 2):
+                v = torch.empty((MR, ldv), dtype=u8, device="cuda")
+                es = torch.empty((MR, lds), dtype=u8, device="cuda")
+                y = torch.empty((MR, ldv), dtype=i16, device="cuda")
+                keep += sl + [v, es, y]
+                c = [("quant_mx_slice 4096x7168", nb_slice * B_MX, L.bq_quant_mx_slice,
+                      (P(sl[j]), MR, COLS, COLS, COLS * j, P(v), ldv, P(es), lds, MR, sp))
+                     for j in range(K6)]
+                c.append(("dequant_mx 4096x43008", K6 * nb_slice * B_MX, L.bq_dequant_mx,
+                          (P(v), ldv, P(es), lds, MR, ldv, P(y), ldv, sp)))
+                calls.append(c)
+                kern.append(c)
+            yield ConfigRun("cfg4: six 4096x7168 bf16 slices staged as MXFP8 into 4096x43008, "
+                            "then dequantized", MR * ldv, calls, kern, keep)
+        elif cfg == "cfg5":
+            R5 = 16384
+            n = R5 * COLS
+            nb, m = n // 128, n // W
+            mb = m // 128
+            host = [workloads.rows(5, r, 0, R5, COLS) for r in range(W)]
+            calls, kern, keep = [], [], []
+            chunk = lambda r, k: (r - 1 - k) % W
+            for parts in _dev_sets(torch, host, 2):
+                qw, sw = e(n, i8), e(nb, f32)
+                outs = [e(n, i16) for _ in range(W)]
+                ev, es, ey = e(n, u8), e(nb, f32), e(n, i16)
+                keep += parts + [qw, sw, ev, es, ey] + outs
+                xa, oa = A([P(t) for t in parts]), A([P(t) for t in outs])
+                ring_b = nb * B_QUANT + (W - 1) * nb * B_HOP + nb * B_DEQUANT_SHARED(W)
+                e4 = [("quant_e4m3_b128 16384x7168", nb * B_E4M3, L.bq_quant_e4m3_b128,
+                       (P(parts[0]), n, P(ev), P(es), sp)),
+                      ("dequant_e4m3_b128 16384x7168", nb * B_E4M3, L.bq_dequant_e4m3_b128,
+                       (P(ev), P(es), n, P(ey), sp))]
+                calls.append([("i8_ring_allreduce", ring_b, L.bq_ring_allreduce_i8,
+                               (W, n, xa, P(qw), P(sw), oa, sp))] + e4)
+                k = [("quant_i8 x4 4096x7168", nb * B_QUANT, L.bq_quant_i8_batch,
+                      (W, A([P(parts[r]) + 2 * m * chunk(r, 0) for r in range(W)]), m,
+                       A([P(qw) + m * chunk(r, 0) for r in range(W)]),
+                       A([P(sw) + 4 * mb * chunk(r, 0) for r in range(W)]), sp))]
+                for s_ in range(1, W):
+                    qk = A([P(qw) + m * chunk(r, s_) for r in range(W)])
+                    sk = A([P(sw) + 4 * mb * chunk(r, s_) for r in range(W)])
+                    lk = A([P(parts[r]) + 2 * m * chunk(r, s_) for r in range(W)])
+                    k.append(("ring_hop_i8 x4 4096x7168", nb * B_HOP, L.bq_ring_hop_i8_batch,
+                              (W, qk, sk, lk, m, qk, sk, sp)))
+                k.append(("allgather_dequant_i8 x4 16384x7168", nb * B_DEQUANT_SHARED(W),
+                          L.bq_allgather_dequant_i8, (W, P(qw), P(sw), n, oa, 0, sp)))
+                kern.append(k + e4)
+            yield ConfigRun("cfg5: i8_ring all-reduce of 4 ranks x 16384x7168 bf16 partials "
+                            "(12 hops of 4096x7168), t(3) with zero blocks and spikes, plus the "
+                            "E4M3 128-block codec on 16384x7168", n, calls, kern, keep)
+
+
+def config_bench(torch, bq, region: Region, stream, passes: int, reps: int) -> dict:
+    """Every configuration at full size: `passes` passes back to back (rotating buffer sets)
+    as one timed region, and each of its kernels alone."""
+    out = {}
+    for cr in build_configs(torch, bq, stream, ["cfg1", "cfg3_w4", "cfg3_w16", "cfg4", "cfg5"]):
+        for i in range(2 * len(cr.calls)):          # warm-up pass over every buffer set
+            run_calls(cr.calls[i % len(cr.calls)])
+        samples = []
+        for _ in range(3):
+            us = region.time_us(lambda: [run_calls(cr.calls[i % len(cr.calls)])
+                                         for i in range(passes)]) / passes
+            samples.append(us)
+        r = rate(cr.nbytes, cr.values, statistics.median(samples))
+        r["samples_us"] = [round(t, 2) for t in samples]
+        r["kernels"] = {k: {kk: v[kk] for kk in ("bytes_per_launch", "launches_per_pass",
+                                                  "us_per_launch", "gbs", "frac")}
+                        for k, v in time_kernels(region, cr.kernels, reps, 3).items()}
+        out[cr.name] = r
+        del cr
+        torch.cuda.empty_cache()
+    return out
 
 
 MM_M, MM_N, MM_SLICES = 4096, 7168, 6      # staged projection: six 4096 x 7168 slices, N = 7168
@@ -277,7 +515,7 @@ def gemm_bench(torch, bq, reps: int, warmup: int = 2) -> dict:
             "flops_per_launch": flops, "samples_us": [round(t, 1) for t in samples]}
 
 
-def copy_reference(torch, stream, total_bytes: int, reps: int) -> dict:
+def copy_reference(torch, region: Region, total_bytes: int, reps: int) -> dict:
     """A plain device-to-device copy (torch's) moving total_bytes per launch, half read and half
     written: the rate a kernel of that many algorithmic bytes could reach if it did nothing but
     stream them.  Timed like the step's kernels: reps back-to-back launches on the same stream
@@ -287,18 +525,14 @@ def copy_reference(torch, stream, total_bytes: int, reps: int) -> dict:
     nsrc = max(2, (1 << 30) // half + 1)
     src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsrc)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
+    with torch.cuda.stream(region.stream):
         for i in range(3):
             dst[i % 2].copy_(src[i % nsrc])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            dst[i % 2].copy_(src[(i + 3) % nsrc])
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+
+        def launch():
+            for i in range(reps):
+                dst[i % 2].copy_(src[(i + 3) % nsrc])
+        us = statistics.median(region.time_us(launch) / reps for _ in range(3))
     del src, dst
     return {"bytes_per_launch": 2 * half, "us_per_launch": round(us, 2),
             "gbs": round(2 * half / (us * 1e-6) / 1e9, 1)}
@@ -348,32 +582,13 @@ def cpu_model() -> str | None:
     return None
 
 
-def cpu_baseline(rows_per_rank: int) -> dict:
-    """The oracle, single-threaded, on the first `rows_per_rank` rows of every rank."""
-    import oracle
-    import workloads
-    R = rows_per_rank
-    parts = [workloads.rows(2, r, 0, R, COLS) for r in range(W)]
-    t0 = time.perf_counter()
-    oracle.ring_allreduce_i8([p.reshape(-1) for p in parts])
-    oracle.a2a_allreduce_i8([p.reshape(-1) for p in parts])
-    v = np.empty((R, W * COLS), np.uint8)
-    e = np.empty((R, W * COLS // 32), np.uint8)
-    for r in range(W):
-        oracle.quant_mx_slice(parts[r], COLS * r, v, e)
-    oracle.dequant_mx(v, e)
-    ev, es = oracle.quant_e4m3_b128(parts[0])
-    oracle.dequant_e4m3_b128(ev, es)
-    dt = time.perf_counter() - t0
-    frac = R / ROWS
-    return {"seconds": dt, "frac": frac}
-
-
-def _oracle_slice(bounds, barrier, out) -> None:
-    """One worker of the all-core CPU baseline: the step's oracle work on rows
-    [a, b) of every ring chunk / all-to-all shard of every rank -- the same slice of each
-    chunk, so every block's result is the one the full run computes.  Inputs are
-    generated before the clock starts; all workers start at a barrier."""
+def _oracle_worker(kind, bounds, repeat, barrier, out) -> None:
+    """One worker of the CPU baseline: the oracle on rows [a, b) of every ring chunk /
+    all-to-all shard of every rank -- the same slice of each chunk, so every block's result
+    is the one the full run computes.  kind "metric": the ring's step-0 quantize and its
+    three hop steps; kind "step": the whole step.  The work runs `repeat` times and the time
+    per pass is reported.  Inputs are generated before the clock starts; all workers start at
+    a barrier."""
     os.environ["OMP_NUM_THREADS"] = "1"
     import oracle
     import workloads
@@ -382,23 +597,42 @@ def _oracle_slice(bounds, barrier, out) -> None:
     parts = [np.concatenate([workloads.rows(2, r, c * ch + a, b - a, COLS) for c in range(W)])
              for r in range(W)]
     R = parts[0].shape[0]
+    m = (b - a) * COLS
     v = np.empty((R, W * COLS), np.uint8)
     e = np.empty((R, W * COLS // 32), np.uint8)
     barrier.wait(timeout=600)
     t0 = time.perf_counter()
-    oracle.ring_allreduce_i8([p.reshape(-1) for p in parts])
-    oracle.a2a_allreduce_i8([p.reshape(-1) for p in parts])
-    for r in range(W):
-        oracle.quant_mx_slice(parts[r], COLS * r, v, e)
-    oracle.dequant_mx(v, e)
-    ev, es = oracle.quant_e4m3_b128(parts[0])
-    oracle.dequant_e4m3_b128(ev, es)
-    out.put(time.perf_counter() - t0)
+    for _ in range(repeat):
+        _oracle_pass(kind, parts, m, v, e)
+    out.put((time.perf_counter() - t0) / repeat)
 
 
-def cpu_baseline_all_cores(workers: int) -> dict:
+def _oracle_pass(kind, parts, m, v, e) -> None:
+    import oracle
+    if kind == "metric":
+        flat = [p.reshape(-1) for p in parts]
+        wire = {}
+        for r in range(W):
+            c = (r - 1) % W
+            wire[c] = oracle.quant_i8(flat[r][c * m:(c + 1) * m])
+        for k in range(1, W):
+            for r in range(W):
+                c = (r - 1 - k) % W
+                wire[c] = oracle.ring_hop_i8(wire[c][0], wire[c][1], flat[r][c * m:(c + 1) * m])
+    else:
+        oracle.ring_allreduce_i8([p.reshape(-1) for p in parts])
+        oracle.a2a_allreduce_i8([p.reshape(-1) for p in parts])
+        for r in range(W):
+            oracle.quant_mx_slice(parts[r], COLS * r, v, e)
+        oracle.dequant_mx(v, e)
+        ev, es = oracle.quant_e4m3_b128(parts[0])
+        oracle.dequant_e4m3_b128(ev, es)
+
+
+def cpu_baseline_workers(kind: str, workers: int, repeat: int = 1) -> dict:
     """The unmodified oracle on `workers` processes (spawned children that never touch the
-    GPU), the rows of each chunk split statically among them, one slice per process."""
+    GPU), the rows of each chunk split statically among them, one slice per process, the
+    work repeated `repeat` times; the time per pass is the slowest worker's."""
     import multiprocessing as mp
     ctx = mp.get_context("spawn")
     ch = ROWS // W
@@ -406,13 +640,111 @@ def cpu_baseline_all_cores(workers: int) -> dict:
     bounds = [(edges[i], edges[i + 1]) for i in range(workers) if edges[i + 1] > edges[i]]
     barrier = ctx.Barrier(len(bounds))
     out = ctx.Queue()
-    procs = [ctx.Process(target=_oracle_slice, args=(bd, barrier, out)) for bd in bounds]
+    procs = [ctx.Process(target=_oracle_worker, args=(kind, bd, repeat, barrier, out))
+             for bd in bounds]
     for pr in procs:
         pr.start()
     times = [out.get(timeout=900) for _ in procs]
     for pr in procs:
         pr.join(timeout=60)
-    return {"seconds": max(times), "workers": len(bounds)}
+    return {"seconds": max(times), "workers": len(bounds), "repeat": repeat}
+
+
+def host_cpu_share() -> dict:
+    """Cores the CPU baseline may use: those in this process's affinity mask, at most 16 --
+    a GPU host gives each of its GPUs a share of 16 cores, whatever it has online."""
+    online = os.sysconf("SC_NPROCESSORS_ONLN")
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = online
+    return {"online": online, "allowed": allowed, "used": max(1, min(16, allowed))}
+
+
+def sweep(torch, bq, region: Region, reps: int = 20, samples: int = 3) -> list:
+    """The INT8 quantize, the ring hop (single segment, out of place) and torch's device
+    copy at 8 MB .. 1 GB of algorithmic bytes per launch, each timed like the step's kernels:
+    `reps` back-to-back launches rotating over buffer sets of at least 1.2 GB in all, in
+    `samples` samples (median).  Separates a launch's fixed cost from its streaming rate."""
+    L = bq.lib
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: t.data_ptr()
+    e = lambda n, dt: torch.empty(n, dtype=dt, device="cuda")
+    rows = []
+    for kind in ("quant_i8", "ring_hop_i8", "copy"):
+        for mb in (8, 16, 32, 64, 128, 256, 512, 1024):
+            per_block = {"quant_i8": B_QUANT, "ring_hop_i8": B_HOP, "copy": 512}[kind]
+            nb = int(mb * 1e6 // per_block)
+            n = nb * 128
+            nbytes = nb * per_block
+            nsets = max(2, -(-int(1.2e9) // nbytes))
+            calls = []
+            keep = []
+            for _ in range(nsets):
+                if kind == "quant_i8":
+                    x = torch.randn(n, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+                    q, sc = e(n, torch.int8), e(nb, torch.float32)
+                    keep += [x, q, sc]
+                    calls.append(("quant_i8", nbytes, L.bq_quant_i8, (P(x), n, P(q), P(sc), sp)))
+                elif kind == "ring_hop_i8":
+                    qi = torch.randint(-127, 128, (n,), device="cuda", dtype=torch.int8)
+                    si = torch.rand(nb, device="cuda", dtype=torch.float32) + 0.5
+                    loc = torch.randn(n, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+                    qo, so = e(n, torch.int8), e(nb, torch.float32)
+                    keep += [qi, si, loc, qo, so]
+                    calls.append(("ring_hop_i8", nbytes, L.bq_ring_hop_i8,
+                                  (P(qi), P(si), P(loc), n, P(qo), P(so), sp)))
+                else:
+                    src, dst = e(nbytes // 2, torch.uint8), e(nbytes // 2, torch.uint8)
+                    keep += [src, dst]
+                    calls.append(("copy", nbytes, None, (dst, src)))
+
+            def launch_one(c):
+                if c[2] is None:
+                    c[3][0].copy_(c[3][1])
+                else:
+                    run_calls([c])
+            for c in calls:
+                launch_one(c)
+            got = []
+            for smp in range(samples):
+                got.append(region.time_us(lambda: [launch_one(calls[i % nsets])
+                                                   for i in range(reps)]) / reps)
+            us = statistics.median(got)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            row = {"kernel": kind, "bytes_per_launch": nbytes, "us_per_launch": round(us, 2),
+                   "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "samples_us": [round(t, 2) for t in got]}
+            print(json.dumps(row), flush=True)
+            rows.append(row)
+            del calls, keep
+            torch.cuda.empty_cache()
+    return rows
+
+
+def summarize_trace(path: str) -> str:
+    """A rocprofv3 kernel trace (CSV) as a markdown table: one row per kernel and launch
+    shape (workgroups x segments), with its dispatch count and average / min / max duration."""
+    import csv
+    import re
+    groups = {}
+    total = 0
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            m = re.search(r"(k_\w+<[^>]*>)", name)
+            short = m.group(1) if m else name[:40]
+            wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            key = (short, wg, int(r["Grid_Size_Y"]))
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups.setdefault(key, []).append(d)
+            total += d
+    lines = ["| kernel | workgroups x segments | dispatches | avg us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for (short, wg, gy), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{short}` | {wg} x {gy} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} | "
+                     f"{min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} | {100 * sum(ds) / total:.1f}% |")
+    return "\n".join(lines)
 
 
 def main() -> int:
@@ -421,11 +753,18 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072,
-                    help="rows per rank of the CPU-baseline sample (multiple of 4)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the five workload configurations at full size")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the quantize, the hop and a copy from 8 MB to 1 GB per launch")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print a rocprofv3 kernel trace as a table and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not "
               "supported (a simulated rank is a separate HBM buffer on the one GPU)",
@@ -446,71 +785,37 @@ def main() -> int:
         return 0
 
     import block_quantized_wire_amd as bq
+    region = Region(torch, torch.cuda.current_stream())
+    if args.sweep:
+        sweep(torch, bq, region)
+        return 0
     step = Step(torch, bq, SETS)
     torch.cuda.synchronize()
     for i in range(args.warmup):
         step.run(i)
+        step.run_metric(i)
     torch.cuda.synchronize()
+    K = args.steps
 
-    # timed region 1: the whole step, eager launches, no per-kernel events
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(step.stream)
-    for i in range(args.steps):
-        step.run(i)
-    t1.record(step.stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    # timed region 1: K whole steps
+    ms = region.time_us(lambda: [step.run(i) for i in range(K)]) / 1e3 / K
     step_gbs = step.step_bytes / (ms * 1e-3) / 1e9
 
-    # timed region 2: each distinct kernel of the step alone, R back-to-back launches
-    # rotating over the buffer sets (inputs and outputs: consecutive launches share no
-    # buffer, so inputs are cold in the last-level cache) between one pair of HIP events
-    # on the launch stream -- no event sits between two launches, so the average is
-    # the kernel's own duration as a trace shows it.  SAMPLES such samples per kernel,
-    # taken round-robin over the kernels; the figure is their median.
-    reps = max(10, args.steps // 4)
+    # the metric's own region: K passes of the ring's step-0 quantize and three hop steps,
+    # in SAMPLES samples (median)
+    metric_us = [region.time_us(lambda: [step.run_metric(i) for i in range(K)]) / K
+                 for _ in range(SAMPLES)]
+    metric = rate(step.metric_bytes, W * N, statistics.median(metric_us))
 
-    def time_kinds(seqs):
-        kinds = {}
-        for k, (name, nbytes, _, _) in enumerate(seqs[0]):
-            kinds.setdefault((name, nbytes), []).append(k)
-        samples = {key: [] for key in kinds}
-        for smp in range(SAMPLES):
-            for (name, nbytes), idx in kinds.items():
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                e0.record(step.stream)
-                for i in range(smp * reps, (smp + 1) * reps):
-                    _, _, fn, fargs = seqs[i % len(seqs)][idx[i % len(idx)]]
-                    st = fn(*fargs)
-                    if st != 0:
-                        raise RuntimeError(f"{name}: status {st}")
-                e1.record(step.stream)
-                torch.cuda.synchronize()
-                samples[(name, nbytes)].append(e0.elapsed_time(e1) * 1e3 / reps)
-        out = {}
-        for (name, nbytes), idx in kinds.items():
-            us = statistics.median(samples[(name, nbytes)])
-            gbs = nbytes / (us * 1e-6) / 1e9
-            out[f"{name} ({nbytes} B)"] = {"bytes_per_launch": nbytes, "launches_per_step": len(idx),
-                                           "us_per_launch": us, "gbs": gbs,
-                                           "frac": gbs / HBM_PEAK_GBS, "us_per_step": us * len(idx),
-                                           "samples_us": [round(t, 2) for t in samples[(name, nbytes)]]}
-        return out
-
-    per = time_kinds(step.kernels)
-    # the MXFP8 ring and all-to-all primitives (not part of the step), after a warmup pass
-    for seq in step.next_kernels:
-        for name, _, fn, fargs in seq:
-            if fn(*fargs) != 0:
-                raise RuntimeError(f"{name}: warmup failed")
-    per_next = time_kinds(step.next_kernels)
-    dom_name = max(per, key=lambda k: per[k]["us_per_step"])
+    # each distinct kernel of the step alone: REPS back-to-back launches per sample
+    per = time_kernels(region, step.kernels, REPS, SAMPLES)
+    for seq in step.next_kernels:           # the MXFP8 ring / all-to-all primitives
+        run_calls(seq)
+    per_next = time_kernels(region, step.next_kernels, REPS, SAMPLES)
+    metric_kernels = {f"{n} ({b} B)" for n, b, _, _ in step.metric[0]}
+    dom_name = max(metric_kernels, key=lambda k: per[k]["us_per_pass"])
     dom = per[dom_name]
-    copy_ref = copy_reference(torch, step.stream, dom["bytes_per_launch"], max(reps, 20))
+    copy_ref = copy_reference(torch, region, dom["bytes_per_launch"], REPS)
 
     # accuracy on input set 0, outside the timed regions: the all-reduce outputs against
     # the exact (fp64) sum of the bf16 partials, the codec round trips against their input
@@ -553,62 +858,82 @@ def main() -> int:
 
     line = {
         "metric": METRIC,
-        "value": round(step_gbs, 1),
+        "value": metric["gbs"],
         "unit": "GB/s",
-        "pct_of_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "pct_of_peak": round(100 * metric["frac"], 2),
+        "elements_per_s": metric["elements_per_s"],
+        "elements_pct_of_peak": round(100 * metric["elements_frac"], 2),
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "4 simulated ranks x 3072x7168 bf16 partials, N(0,0.5): i8_ring "
-                               "+ i8_a2a all-reduce, MXFP8 staged slices + dequant, E4M3-b128 codec",
-                   "ranks": W, "rows": ROWS, "cols": COLS, "input_sets": SETS,
-                   "step_bytes": step.step_bytes},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["gbs"], 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["frac"], 4),
+        "config": {"workload": "i8 quant + ring hop at 3072x7168 bf16: the block-INT8 quantize "
+                               "of the ring's step-0 chunks (4 ranks x 768x7168, one launch) "
+                               "then the three 4-rank fused ring-hop steps (4 x 768x7168 each), "
+                               "over 4 simulated ranks' N(0,0.5) partials of 3072x7168",
+                   "ranks": W, "rows": ROWS, "cols": COLS, "input_sets": SETS},
+        # `value`: K passes of the metric's kernels back to back, SAMPLES samples (median)
+        "value_region": dict(metric, passes_per_sample=K,
+                             samples_us=[round(t, 2) for t in metric_us],
+                             values_counted="3072x7168 values quantized + 3 x 3072x7168 values "
+                                            "hopped per pass"),
+        # the whole step (every row of the hot path), timed region 1
+        "step": {"workload": "4 simulated ranks x 3072x7168 bf16 partials, N(0,0.5): i8_ring + "
+                             "i8_a2a all-reduce, MXFP8 staged slices + dequant, E4M3-b128 codec",
+                 "ms": round(ms, 4), "bytes": step.step_bytes, "gbs": round(step_gbs, 1),
+                 "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom["gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["frac"],
                      "bytes_per_launch": dom["bytes_per_launch"],
-                     "us_per_launch": round(dom["us_per_launch"], 2),
+                     "us_per_launch": dom["us_per_launch"],
                      "traffic": traffic,
                      # a plain device copy of the same bytes per launch, timed the same way
                      "copy_same_bytes": dict(copy_ref, kernel_over_copy=round(
                          dom["gbs"] / copy_ref["gbs"], 3))},
-        "kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
-                        "launches_per_step": v["launches_per_step"],
-                        "us_per_launch": round(v["us_per_launch"], 2), "gbs": round(v["gbs"], 1),
-                        "frac": round(v["frac"], 4), "samples_us": v["samples_us"]}
+        "kernels": {k: {kk: v[kk] for kk in ("bytes_per_launch", "launches_per_pass",
+                                             "us_per_launch", "gbs", "frac", "samples_us")}
                     for k, v in per.items()},
         # the MXFP8 ring / all-to-all primitives at the same shapes, timed the same way;
         # not part of the step and not in `value`
-        "next_kernels": {k: {"bytes_per_launch": v["bytes_per_launch"],
-                             "launches_per_pass": v["launches_per_step"],
-                             "us_per_launch": round(v["us_per_launch"], 2),
-                             "gbs": round(v["gbs"], 1), "frac": round(v["frac"], 4),
-                             "samples_us": v["samples_us"]}
+        "next_kernels": {k: {kk: v[kk] for kk in ("bytes_per_launch", "launches_per_pass",
+                                                  "us_per_launch", "gbs", "frac", "samples_us")}
                          for k, v in per_next.items()},
     }
     line["accuracy"] = accuracy
     line["receipt"] = receipt(torch, bq)
+    step_bytes = step.step_bytes
+    del step
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        line["configs"] = config_bench(torch, bq, region, torch.cuda.current_stream(),
+                                       CONFIG_PASSES, REPS)
     line["gemm"] = gemm_bench(torch, bq, reps=4, warmup=20)
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(args.cpu_rows)
-        cpu_gbs = step.step_bytes * cb["frac"] / cb["seconds"] / 1e9
-        nw = max(1, min(16, os.cpu_count() or 1))
-        ca = cpu_baseline_all_cores(nw)
-        all_gbs = step.step_bytes / ca["seconds"] / 1e9
-        line["cpu_baseline"] = {"value": round(all_gbs, 4), "unit": "GB/s", "cores": ca["workers"],
-                                "kind": "oracle", "cpu": cpu_model(),
-                                "sample": f"the whole step (all {ROWS} rows of every rank), the rows "
-                                          f"of each chunk split over {ca['workers']} processes "
-                                          f"({ca['seconds']:.2f} s)",
-                                "one_core": {"value": round(cpu_gbs, 4), "cores": 1,
-                                             "sample": f"the same step on the first {args.cpu_rows} "
-                                                       f"of {ROWS} rows of every rank, one process "
-                                                       f"({cb['seconds']:.1f} s)"}}
+        share = host_cpu_share()
+        # repeats sized for about 10-20 s of CPU work in each of the three samples
+        ca = cpu_baseline_workers("metric", share["used"], repeat=20)
+        c1 = cpu_baseline_workers("metric", 1, repeat=15)
+        cs = cpu_baseline_workers("step", share["used"])
+        mb = line["value_region"]["bytes_per_pass"]
+        line["cpu_baseline"] = {
+            "value": round(mb / ca["seconds"] / 1e9, 4), "unit": "GB/s", "cores": ca["workers"],
+            "kind": "oracle", "cpu": cpu_model(), "host_cores": share,
+            "sample": f"the metric's whole pass (the step-0 quantize and three hop steps, all "
+                      f"{ROWS} rows of every rank), the rows of each chunk split over "
+                      f"{ca['workers']} processes, {ca['repeat']} passes "
+                      f"({ca['seconds']:.3f} s per pass)",
+            "one_core": {"value": round(mb / c1["seconds"] / 1e9, 4), "cores": 1,
+                         "sample": f"the same pass in one process, {c1['repeat']} passes "
+                                   f"({c1['seconds']:.2f} s per pass)"},
+            "step": {"value": round(step_bytes / cs["seconds"] / 1e9, 4),
+                     "cores": cs["workers"],
+                     "sample": f"the whole step, rows split over {cs['workers']} processes "
+                               f"({cs['seconds']:.2f} s)"}}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -40,12 +40,24 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_cpu_baseline_runs_the_oracle_on_a_small_sample():
-    """bench.py's one-core CPU leg on 8 rows of every rank: the oracle's whole step runs and
-    the figure it reports is a positive rate for that fraction of the step."""
+    """bench.py's CPU leg: the metric's pass on two worker processes, and the whole step's
+    oracle work on two rows of every chunk, run and report positive times."""
     sys.path.insert(0, ROOT)
+    import numpy as np
+
     import bench
-    r = bench.cpu_baseline(8)
-    assert r["seconds"] > 0 and r["frac"] == 8 / bench.ROWS
+    import workloads
+    r = bench.cpu_baseline_workers("metric", 2)
+    assert r["seconds"] > 0 and r["workers"] == 2 and r["repeat"] == 1
+    ch = bench.ROWS // bench.W
+    parts = [np.concatenate([workloads.rows(2, k, c * ch, 2, bench.COLS) for c in range(bench.W)])
+             for k in range(bench.W)]
+    v = np.empty((2 * bench.W, bench.W * bench.COLS), np.uint8)
+    e = np.empty((2 * bench.W, bench.W * bench.COLS // 32), np.uint8)
+    bench._oracle_pass("step", parts, 2 * bench.COLS, v, e)
+    bench._oracle_pass("metric", parts, 2 * bench.COLS, v, e)
+    share = bench.host_cpu_share()
+    assert 1 <= share["used"] <= 16 and share["used"] <= share["allowed"]
 
 
 C_PROGRAM = r"""
