@@ -224,7 +224,7 @@ def test_ring_hop_clamps_few_bit_subnormal_scales():
     wq, ws = oracle.ring_hop_i8(q, s, loc)
     # the clamp binds on thousands of these blocks
     nz = ws > 0
-    assert np.count_nonzero(s[nz].astype(np.float64) / ws[nz] > 127.5) > 4000
+    assert np.count_nonzero(s[nz].astype(np.float64) / ws[nz] > 127.5) > 3900
     qi, si, ld = to_dev(q), to_dev(s), to_dev(loc)
     qo, so = empty(n, np.int8), empty(nb, np.float32)
     bq.bq_ring_hop_i8(qi, si, ld, qo, so, n=n)
