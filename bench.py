@@ -19,14 +19,15 @@ algorithmic bytes (each kernel's inputs read once, outputs written once) over ti
 in GB/s against the 8 TB/s HBM peak.  The whole step is reported beside it
 (`step`), and so is every distinct kernel of the step alone (`kernels`), each of
 the five workload configurations at full size (`configs`) and the staged MXFP8
-GEMM (`gemm`).  Inputs are resident in HBM.  Four complete buffer sets (inputs,
-intermediates, outputs; about 1 GB each) rotate pass by pass, so a pass's inputs
-are cold in the 256 MB last-level cache while what a kernel consumes from the
-previous kernel of the same pass may be served by it, as in any pipeline on one GPU.
+GEMM (`gemm`).  Inputs are resident in HBM.  Sixteen complete buffer sets (inputs,
+intermediates, outputs; about 1.5 GB each) rotate pass by pass -- and launch by launch
+when a kernel is timed alone -- so inputs are cold in the 256 MB last-level cache while
+what a kernel consumes from the previous kernel of the same pass may be served by it,
+as in any pipeline on one GPU.
 
-Every timed region starts behind a 1 GiB device copy queued on the same stream, so
-the host has enqueued the region's launches before the GPU reaches them: the events
-then bracket GPU work only, with no gap waiting for the host.
+Every timed region starts behind a 2 GiB read queued on the same stream, so the host has
+enqueued the region's launches before the GPU reaches them: the events then bracket GPU
+work only, with no gap waiting for the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --sweep             (quantize, hop and copy from 8 MB to 1 GB)
@@ -55,9 +56,10 @@ ROWS, COLS = 3072, 7168
 N = ROWS * COLS
 NB = N // 128
 M = N // W                 # values per ring chunk / A2A shard
-SETS = 4                   # rotating buffer sets, each a full step's inputs and outputs (~1 GB)
+SETS = 16                  # rotating buffer sets, each a full step's inputs and outputs (~1.5 GB)
+DRAWS = 4                  # distinct input draws; set k holds draw k % DRAWS at its own addresses
 SAMPLES = 5                # timed samples per region (median reported)
-REPS = 20                  # back-to-back launches per sample when a kernel is timed alone
+REPS = 30                  # back-to-back launches per sample when a kernel is timed alone
 CONFIG_PASSES = 10         # passes per sample of each workload configuration
 
 # algorithmic bytes per 128 values of each kernel (inputs read once, outputs written once)
@@ -112,8 +114,12 @@ class Step:
         e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
         self.sets = []
         for k in range(sets):
-            b = {"parts": [torch.from_numpy(workloads.rows(2, r + 16 * k, 0, ROWS, COLS)
-                                            .view(np.int16)).to(dev) for r in range(W)]}
+            if k < DRAWS:
+                parts = [torch.from_numpy(workloads.rows(2, r + 16 * k, 0, ROWS, COLS)
+                                          .view(np.int16)).to(dev) for r in range(W)]
+            else:
+                parts = [t.clone() for t in self.sets[k % DRAWS]["parts"]]
+            b = {"parts": parts}
             b["q_wire"], b["s_wire"] = e(N, i8), e(NB, f32)
             b["ring_out"] = [e(N, i16) for _ in range(W)]
             b["q_send"] = [e(N, i8) for _ in range(W)]
@@ -253,16 +259,17 @@ def run_calls(calls) -> None:
 
 
 class Region:
-    """Timing of launches on one stream between two HIP events.  A 1 GiB device copy is
-    queued first, on the same stream: it keeps the GPU busy for about 0.3 ms while the
-    host enqueues the region's launches, so the GPU never waits for the host inside the
-    region and the events bracket GPU work only.  It also evicts the 256 MB last-level
-    cache, so the region's first inputs are cold."""
+    """Timing of launches on one stream between two HIP events.  A read of 2 GiB (a sum) is
+    queued first, on the same stream: it keeps the GPU busy for about half a millisecond
+    while the host enqueues the region's launches, so the GPU never waits for the host
+    inside the region and the events bracket GPU work only.  Being a read, it also leaves
+    the 256 MB last-level cache holding only clean lines of its own -- the region's first
+    inputs are cold and no earlier write is still waiting to be written back (a copy
+    there instead measurably slowed the first launches of each region)."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
-        self.src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        self.dst = torch.empty_like(self.src)
+        self.src = torch.zeros(1 << 29, dtype=torch.float32, device="cuda")
 
     def time_us(self, launch) -> float:
         """Microseconds from the first to the last of the launches `launch()` enqueues."""
@@ -271,7 +278,7 @@ class Region:
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(self.stream):
-            self.dst.copy_(self.src)
+            self.total = self.src.sum()
         e0.record(self.stream)
         launch()
         e1.record(self.stream)
@@ -303,6 +310,39 @@ def time_kernels(region: Region, seqs, reps: int, samples: int) -> dict:
                                        "frac": round(gbs / HBM_PEAK_GBS, 4),
                                        "us_per_pass": us * len(idx),
                                        "samples_us": [round(t, 2) for t in got[(name, nbytes)]]}
+    return out
+
+
+def metric_split(torch, region: Region, step, passes: int) -> dict:
+    """The metric's pass with a HIP event before every launch and after the last: each
+    kernel's duration inside the pipeline (its inputs as the previous kernel left them),
+    averaged over `passes` passes, and the region's total against the plain region."""
+    calls = step.metric
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls[0]) + 1)]
+          for _ in range(passes)]
+
+    def launch():
+        for i in range(passes):
+            for j, c in enumerate(calls[i % len(calls)]):
+                ev[i][j].record(region.stream)
+                run_calls([c])
+            ev[i][-1].record(region.stream)
+    region.time_us(launch)
+    per_pos = [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(passes)]
+               for j in range(len(calls[0]))]
+    kernels = {}
+    for j, (name, nbytes, _, _) in enumerate(calls[0]):
+        kernels.setdefault(f"{name} ({nbytes} B)", []).extend(per_pos[j])
+    out = {"kernels": {}, "positions_us": [round(statistics.mean(p), 2) for p in per_pos],
+           "pass_us": round(sum(statistics.mean(p) for p in per_pos), 2)}
+    for key, ds in kernels.items():
+        nbytes = int(key.rsplit("(", 1)[1].split()[0])
+        us = statistics.mean(ds)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        n = len(ds) // passes
+        out["kernels"][key] = {"bytes_per_launch": nbytes, "launches_per_pass": n,
+                               "us_per_launch": round(us, 2), "us_per_pass": us * n,
+                               "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     return out
 
 
@@ -348,10 +388,10 @@ def build_configs(torch, bq, stream, which):
     i16, i8, u8, f32 = torch.int16, torch.int8, torch.uint8, torch.float32
     for cfg in which:
         if cfg == "cfg1":
-            # block-INT8 round trip of one 512x7168 tensor; 28 buffer sets (~0.5 GB)
+            # block-INT8 round trip of one 512x7168 tensor; 56 buffer sets (~1 GB)
             R1, n = 512, 512 * COLS
             nb = n // 128
-            sets = 28
+            sets = 56
             xs = _dev_sets(torch, [workloads.rows(1, 0, 0, R1, COLS)], sets)
             calls, kern, keep = [], [], []
             for (x,) in xs:
@@ -723,27 +763,56 @@ def sweep(torch, bq, region: Region, reps: int = 20, samples: int = 3) -> list:
 
 
 def summarize_trace(path: str) -> str:
-    """A rocprofv3 kernel trace (CSV) as a markdown table: one row per kernel and launch
-    shape (workgroups x segments), with its dispatch count and average / min / max duration."""
+    """A rocprofv3 kernel trace (CSV) as markdown: one row per kernel and launch shape
+    (workgroups x segments) with its dispatch count, average / min / max duration and the
+    average over its back-to-back runs (10 or more consecutive dispatches of that kernel and
+    shape: the per-kernel samples); then the metric's passes (the INT8 quantize of 1344 x 4
+    workgroups followed by three ring hops of the same shape) with the average duration of
+    each of the four launches."""
     import csv
     import re
-    groups = {}
-    total = 0
+    rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
             m = re.search(r"(k_\w+<[^>]*>)", name)
             short = m.group(1) if m else name[:40]
             wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
-            key = (short, wg, int(r["Grid_Size_Y"]))
-            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-            groups.setdefault(key, []).append(d)
-            total += d
-    lines = ["| kernel | workgroups x segments | dispatches | avg us | min us | max us | share of GPU time |",
-             "|---|---|---|---|---|---|---|"]
-    for (short, wg, gy), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{short}` | {wg} x {gy} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} | "
-                     f"{min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} | {100 * sum(ds) / total:.1f}% |")
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         (short, wg, int(r["Grid_Size_Y"]))))
+    rows.sort()
+    keys = [k for _, _, k in rows]
+    dur = [(e - s) / 1e3 for s, e, _ in rows]
+    groups, runs = {}, {}
+    for k, d in zip(keys, dur):
+        groups.setdefault(k, []).append(d)
+    i = 0
+    while i < len(keys):
+        j = i
+        while j + 1 < len(keys) and keys[j + 1] == keys[i]:
+            j += 1
+        if j - i + 1 >= 10:
+            runs.setdefault(keys[i], []).extend(dur[i:j + 1])
+        i = j + 1
+    total = sum(dur)
+    lines = ["| kernel | workgroups x segments | dispatches | avg us | min us | max us | "
+             "back-to-back avg us | share of GPU time |", "|---|---|---|---|---|---|---|---|"]
+    for k, ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        b2b = f"{statistics.mean(runs[k]):.2f}" if k in runs else ""
+        lines.append(f"| `{k[0]}` | {k[1]} x {k[2]} | {len(ds)} | {statistics.mean(ds):.2f} | "
+                     f"{min(ds):.2f} | {max(ds):.2f} | {b2b} | {100 * sum(ds) / total:.1f}% |")
+    q = ("k_quant_i8<1>", 1344, 4)
+    h = ("k_ring_hop_i8<1>", 1344, 4)
+    pos = [[], [], [], []]
+    for i in range(len(keys) - 3):
+        if keys[i] == q and keys[i + 1] == h and keys[i + 2] == h and keys[i + 3] == h:
+            for p in range(4):
+                pos[p].append(dur[i + p])
+    if pos[0]:
+        lines += ["", f"Metric passes (quantize, hop 1, hop 2, hop 3): {len(pos[0])}; average us "
+                      f"{', '.join(f'{statistics.mean(p):.2f}' for p in pos)}; hop average "
+                      f"{statistics.mean(pos[1] + pos[2] + pos[3]):.2f}; pass "
+                      f"{sum(statistics.mean(p) for p in pos):.2f}"]
     return "\n".join(lines)
 
 
@@ -806,15 +875,17 @@ def main() -> int:
     metric_us = [region.time_us(lambda: [step.run_metric(i) for i in range(K)]) / K
                  for _ in range(SAMPLES)]
     metric = rate(step.metric_bytes, W * N, statistics.median(metric_us))
+    split = metric_split(torch, region, step, K)
 
     # each distinct kernel of the step alone: REPS back-to-back launches per sample
     per = time_kernels(region, step.kernels, REPS, SAMPLES)
     for seq in step.next_kernels:           # the MXFP8 ring / all-to-all primitives
         run_calls(seq)
     per_next = time_kernels(region, step.next_kernels, REPS, SAMPLES)
-    metric_kernels = {f"{n} ({b} B)" for n, b, _, _ in step.metric[0]}
-    dom_name = max(metric_kernels, key=lambda k: per[k]["us_per_pass"])
-    dom = per[dom_name]
+    # the roofline's kernel: the metric pass's kernel with the most time per pass, timed
+    # inside the metric's own region (events between its launches)
+    dom_name = max(split["kernels"], key=lambda k: split["kernels"][k]["us_per_pass"])
+    dom = split["kernels"][dom_name]
     copy_ref = copy_reference(torch, region, dom["bytes_per_launch"], REPS)
 
     # accuracy on input set 0, outside the timed regions: the all-reduce outputs against
@@ -882,6 +953,8 @@ def main() -> int:
                              samples_us=[round(t, 2) for t in metric_us],
                              values_counted="3072x7168 values quantized + 3 x 3072x7168 values "
                                             "hopped per pass"),
+        # the metric's kernels inside its region (events between launches), per launch
+        "value_split": split,
         # the whole step (every row of the hot path), timed region 1
         "step": {"workload": "4 simulated ranks x 3072x7168 bf16 partials, N(0,0.5): i8_ring + "
                              "i8_a2a all-reduce, MXFP8 staged slices + dequant, E4M3-b128 codec",
@@ -891,6 +964,11 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["frac"],
                      "bytes_per_launch": dom["bytes_per_launch"],
                      "us_per_launch": dom["us_per_launch"],
+                     "launches_per_pass": dom["launches_per_pass"],
+                     "timed": "inside the metric's region: HIP events between its launches, "
+                              "K passes, the kernel's mean duration",
+                     # the same kernel alone, every input cold (per-kernel protocol below)
+                     "alone_cold": {kk: per[dom_name][kk] for kk in ("us_per_launch", "gbs", "frac")},
                      "traffic": traffic,
                      # a plain device copy of the same bytes per launch, timed the same way
                      "copy_same_bytes": dict(copy_ref, kernel_over_copy=round(
