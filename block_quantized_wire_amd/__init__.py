@@ -22,7 +22,8 @@ __all__ = [
     "bq_a2a_reduce_i8",
     "bq_ring_hop_i8",
     "bq_quant_i8_batch", "bq_dequant_i8_batch", "bq_ring_hop_i8_batch",
-    "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_a2a_allreduce_i8",
+    "bq_allgather_dequant_i8", "bq_ring_allreduce_i8", "bq_ring_allreduce_i8_noalloc",
+    "bq_a2a_allreduce_i8",
     "bq_quant_mx", "bq_dequant_mx", "bq_quant_mx_slice", "bq_mx_staging_bytes",
     "bq_quant_mx_f16", "bq_quant_mx_slice_f16", "bq_mm_mx",
     "bq_quant_mx_batch", "bq_dequant_mx_batch", "bq_ring_hop_mx", "bq_ring_hop_mx_batch",
@@ -36,7 +37,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libblockq.s
 
 BQ_OK = 0
 BQ_STATUS = {0: "BQ_OK", 1: "BQ_ERR_NULL", 2: "BQ_ERR_SIZE", 3: "BQ_ERR_ALIGN",
-             4: "BQ_ERR_BOUNDS", 5: "BQ_ERR_NSRC", 6: "BQ_ERR_ALIAS", 7: "BQ_ERR_LAUNCH"}
+             4: "BQ_ERR_BOUNDS", 5: "BQ_ERR_NSRC", 6: "BQ_ERR_ALIAS", 7: "BQ_ERR_LAUNCH",
+             8: "BQ_ERR_SCRATCH"}
 
 
 class BlockqError(RuntimeError):
@@ -61,6 +63,7 @@ _SIGS = {
     "bq_allgather_dequant_i8": [_I, _P, _P, _I64, _PP, _I, _P],
     "bq_ring_allreduce_i8": [_I, _I64, _PP, _P, _P, _PP, _P],
     "bq_a2a_allreduce_i8": [_I, _I64, _PP, _PP, _PP, _P, _P, _P, _PP, _P],
+    "bq_ring_allreduce_i8_noalloc": [_I, _I64, _PP, _PP, _P],
     "bq_quant_mx": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
     "bq_dequant_mx": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
     "bq_quant_mx_slice": [_P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I64, _P],
@@ -224,6 +227,13 @@ def bq_ring_allreduce_i8(partials, q_wire, s_wire, outs, n: int | None = None,
     _check("bq_ring_allreduce_i8",
            _L().bq_ring_allreduce_i8(len(partials), n, _ptrs(partials), _ptr(q_wire), _ptr(s_wire),
                                     _ptrs(outs), _stream(stream)))
+
+
+def bq_ring_allreduce_i8_noalloc(partials, outs, n: int | None = None, stream=None) -> None:
+    n = _numel(partials[0]) if n is None else n
+    _check("bq_ring_allreduce_i8_noalloc",
+           _L().bq_ring_allreduce_i8_noalloc(len(partials), n, _ptrs(partials), _ptrs(outs),
+                                            _stream(stream)))
 
 
 def bq_a2a_allreduce_i8(partials, q_send, s_send, red, q_bcast, s_bcast, outs,

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libblockq.so")
-SOURCES = ["bq_abi.cpp", "bq_i8.hip", "bq_mx.hip", "bq_mxc.hip", "bq_mm.hip"]
+SOURCES = ["bq_abi.cpp", "bq_i8.hip", "bq_mx.hip", "bq_mxc.hip", "bq_mm.hip", "bq_noalloc.hip"]
 HEADERS = ["bq_device.h", "bq_launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

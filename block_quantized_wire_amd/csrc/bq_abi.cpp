@@ -423,6 +423,8 @@ const char* bq_status_str(bq_status s) {
     case BQ_ERR_NSRC: return "a source, rank or segment count is out of range";
     case BQ_ERR_ALIAS: return "an output overlaps an input or another output";
     case BQ_ERR_LAUNCH: return "the HIP kernel launch failed";
+    case BQ_ERR_SCRATCH:
+        return "the call needs more than the allocation-free entry point's scratch array";
     }
     return "unknown status";
 }

@@ -60,7 +60,8 @@ typedef enum bq_status {
     BQ_ERR_BOUNDS = 4,  /* a leading dimension, offset or capacity does not fit */
     BQ_ERR_NSRC = 5,    /* a source / rank / segment count is outside its range */
     BQ_ERR_ALIAS = 6,   /* an output overlaps an input or another output */
-    BQ_ERR_LAUNCH = 7   /* the HIP launch failed */
+    BQ_ERR_LAUNCH = 7,  /* the HIP launch failed */
+    BQ_ERR_SCRATCH = 8  /* the allocation-free entry point's scratch is too small */
 } bq_status;
 
 #define BQ_BLOCK 128        /* values per INT8 / E4M3 block */
@@ -157,6 +158,19 @@ bq_status bq_allgather_dequant_i8(int world, const int8_t* q, const float* s, in
 bq_status bq_ring_allreduce_i8(int world, int64_t n, const uint16_t* const* partials,
                                int8_t* q_wire, float* s_wire, uint16_t* const* out,
                                void* stream);
+
+/* Allocation-free form of bq_ring_allreduce_i8, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Identical arguments, validation and results, except that the wire payload
+ * lives in a library-owned device array of BQ_NOALLOC_SCRATCH_BYTES per GPU (held from
+ * the first call on that GPU until the process ends) instead of caller buffers:
+ * n + 4 * n/128 bytes must fit, else BQ_ERR_SCRATCH (nothing launched); that is at most
+ * 65,075,200 values.  The call allocates nothing.  Every call on one GPU uses that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other threads) race on
+ * it and must be ordered by the caller.  Nothing in the array needs to start at zero. */
+#define BQ_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+bq_status bq_ring_allreduce_i8_noalloc(int world, int64_t n, const uint16_t* const* partials,
+                                       uint16_t* const* out, void* stream);
 
 /* i8_a2a all-reduce (P1 Summary, Implementation): every rank quantizes its partial
  * once into q_send[r]/s_send[r]; owner j dequantizes shard j of the W payloads and

@@ -158,6 +158,29 @@ def test_collective_driver_errors():
     assert L.bq_a2a_allreduce_i8(0, n, parts, qsend, ssend, red, qb, sb, outs, S) == NSRC
 
 
+def test_noalloc_ring_errors():
+    """The allocation-free ring all-reduce checks counts and sizes first -- a call whose
+    wire payload would not fit the library's scratch array fails with BQ_ERR_SCRATCH --
+    then NULL host arrays, before it looks up the scratch array or launches anything."""
+    n = 4 * 1024
+    parts = arr(A, A + 16384, A + 32768, A + 49152)
+    outs = arr(A + 2 ** 20, A + 2 ** 20 + 16384, A + 2 ** 20 + 32768, A + 2 ** 20 + 49152)
+    SCRATCH = 8
+    assert bq.BQ_STATUS[SCRATCH] == "BQ_ERR_SCRATCH"
+    assert b"scratch" in L.bq_status_str(SCRATCH)
+    assert L.bq_ring_allreduce_i8_noalloc(0, n, parts, outs, S) == NSRC
+    assert L.bq_ring_allreduce_i8_noalloc(17, n, parts, outs, S) == NSRC
+    assert L.bq_ring_allreduce_i8_noalloc(4, 128 * 6, parts, outs, S) == SIZE
+    assert L.bq_ring_allreduce_i8_noalloc(4, -512, parts, outs, S) == SIZE
+    assert L.bq_ring_allreduce_i8_noalloc(4, n, None, outs, S) == NULL
+    assert L.bq_ring_allreduce_i8_noalloc(4, n, parts, None, S) == NULL
+    # 64 MiB hold 508400 blocks of 132 bytes: 65,075,200 values
+    most = (64 * 2 ** 20 // 132) * 128
+    assert most == 65075200
+    assert L.bq_ring_allreduce_i8_noalloc(1, most + 128, parts, outs, S) == SCRATCH
+    assert L.bq_ring_allreduce_i8_noalloc(4, 2 ** 40, parts, outs, S) == SCRATCH
+
+
 def test_a2a_reduce_and_allgather_errors():
     n = 1024
     qs = arr(A, A + 4096)
@@ -338,6 +361,7 @@ def test_every_entry_point_accepts_empty_input():
         "bq_ring_hop_i8_batch": lambda: L.bq_ring_hop_i8_batch(1, one, one, one, 0, one, one, S),
         "bq_allgather_dequant_i8": lambda: L.bq_allgather_dequant_i8(3, q, e, 0, two, 1, S),
         "bq_ring_allreduce_i8": lambda: L.bq_ring_allreduce_i8(3, 0, two, q, e, two, S),
+        "bq_ring_allreduce_i8_noalloc": lambda: L.bq_ring_allreduce_i8_noalloc(3, 0, two, two, S),
         "bq_a2a_allreduce_i8": lambda: L.bq_a2a_allreduce_i8(3, 0, two, two, two, y, q, e, two,
                                                              S),
         "bq_quant_mx": lambda: L.bq_quant_mx(p, 0, 256, 256, q, 256, e, 8, S),
