@@ -60,6 +60,8 @@ _SIGS = {
     "orc_a2a_reduce_mx": ([ctypes.c_int, ctypes.c_int, _P, _P, _I64, _P, _P, _P, _P], None),
     "orc_ring_allreduce_mx": ([ctypes.c_int, _I64, _P, _P, _P, _P], None),
     "orc_a2a_allreduce_mx": ([ctypes.c_int, _I64, _P, _P, _P, _P, _P], None),
+    "orc_mx_mfma_offset": ([_I64, _I64, _I64], _I64),
+    "orc_mx_scales_to_mfma": ([_P, _I64, _I64, _I64, _I64, _I64, _P], None),
     "orc_quant_e4m3_b128": ([_P, _I64, _P, _P], None),
     "orc_dequant_e4m3_b128": ([_P, _P, _I64, _P], None),
 }
@@ -282,6 +284,53 @@ def mm_mx(xv: np.ndarray, xe: np.ndarray, wv: np.ndarray, we: np.ndarray):
     Wt = mx_values_f64(wv, we)
     assert X.shape[1] == Wt.shape[1]
     return X @ Wt.T, np.abs(X) @ np.abs(Wt).T
+
+
+# ---- MXFP8 scales in the scaled-MFMA operand order ------------------------------
+
+def mx_mfma_bytes(rows: int, cols: int) -> int:
+    """Bytes of the layout for `rows` rows and `cols` columns: 256-byte tiles of 16 rows x
+    512 columns."""
+    return 256 * (-(-rows // 16)) * (-(-cols // 512))
+
+
+def mx_mfma_offset(row: int, group: int, row_blocks: int) -> int:
+    return lib().orc_mx_mfma_offset(row, group, row_blocks)
+
+
+def mx_scales_to_mfma(e: np.ndarray, out: np.ndarray, row_blocks: int, group_off: int = 0) -> None:
+    """Place row-major scales e (rows, groups) into `out` (uint8, the layout) in place, group
+    g of e at layout group group_off + g; other bytes of `out` are left as they are."""
+    e = _c(e, np.uint8)
+    assert out.dtype == np.uint8 and out.flags.c_contiguous
+    rows, groups = e.shape
+    assert rows <= 16 * row_blocks
+    assert out.size >= 256 * row_blocks * (-(-(group_off + groups) // 16))
+    lib().orc_mx_scales_to_mfma(e.ctypes.data, groups, rows, groups, group_off, row_blocks,
+                                out.ctypes.data)
+
+
+def quant_mx_slice_mfma(x: np.ndarray, col_off: int, v: np.ndarray, e_mfma: np.ndarray,
+                        capacity_rows: int, f16: bool = False) -> None:
+    """The staged slice quantization with the scales in the MFMA layout: values as
+    quant_mx_slice writes them, scale (row, group) of the slice at layout group
+    col_off/32 + group of a layout with ceil(capacity_rows/16) row blocks."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    assert col_off % 128 == 0 and cols % 128 == 0 and rows <= capacity_rows
+    vs, es = (quant_mx_f16 if f16 else quant_mx)(x)
+    v[:rows, col_off:col_off + cols] = vs
+    mx_scales_to_mfma(es, e_mfma, -(-capacity_rows // 16), col_off // 32)
+
+
+def mx_scales_from_mfma(e_mfma: np.ndarray, rows: int, groups: int, row_blocks: int) -> np.ndarray:
+    """Row-major (rows, groups) scales read back from the layout through the offset map."""
+    e_mfma = _c(e_mfma, np.uint8).reshape(-1)
+    out = np.empty((rows, groups), np.uint8)
+    for r in range(rows):
+        for g in range(groups):
+            out[r, g] = e_mfma[mx_mfma_offset(r, g, row_blocks)]
+    return out
 
 
 # ---- MXFP8 on the collective topologies (flat: n E4M3 bytes, n/32 E8M0 bytes) ----

@@ -459,6 +459,34 @@ void orc_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64
 }
 
 /* ---------------------------------------------------------------------- */
+/* MXFP8 scales in the order of the scaled matrix instruction (P4 Behavior: */
+/* the staging holds the scale layout the GEMM consumes).  One 256-byte     */
+/* tile serves 16 rows x 512 columns: the four K steps of 128 columns, each */
+/* needing per lane l the byte of row l%16 and 32-column block l/16.        */
+/* ---------------------------------------------------------------------- */
+
+int64_t orc_mx_mfma_offset(int64_t row, int64_t group, int64_t row_blocks) {
+    int64_t kgroup = group / 16;          /* which 512 columns */
+    int64_t step = (group % 16) / 4;      /* which K step of 128 among the four */
+    int64_t block = group % 4;            /* which 32 columns within the K step */
+    int64_t rblock = row / 16;
+    int64_t lane = 16 * block + row % 16; /* the lane that supplies this byte */
+    int64_t tile = kgroup * row_blocks + rblock;
+    return 256 * tile + 4 * lane + step;
+}
+
+void orc_mx_scales_to_mfma(const uint8_t* e8m0, int64_t lds, int64_t rows, int64_t groups,
+                           int64_t group_off, int64_t row_blocks, uint8_t* out) {
+    if (rows > 16 * row_blocks) {
+        fprintf(stderr, "bq_oracle: more rows than the layout's row blocks hold\n");
+        abort();
+    }
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t g = 0; g < groups; g++)
+            out[orc_mx_mfma_offset(r, group_off + g, row_blocks)] = e8m0[r * lds + g];
+}
+
+/* ---------------------------------------------------------------------- */
 /* MXFP8 on the collective topologies (P2 PR body Summary / Modes: mx_ring  */
 /* and mx_a2a carry the same 132-byte-per-128 payload over the ring and the */
 /* all-to-all, with the INT8 modes' canonical-payload rule).  The tensor is */

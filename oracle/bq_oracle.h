@@ -85,6 +85,20 @@ void orc_quant_mx_slice_f16(const uint16_t* x, int64_t rows, int64_t cols, int64
                             int64_t col_off, uint8_t* v, int64_t ldv, uint8_t* e8m0,
                             int64_t lds);
 
+/* ---- MXFP8 scales in the order of the scaled matrix instruction ---------
+ * P4 Behavior: the caller-owned staging holds the MXFP8 values and the scale layout
+ * the dense GEMM consumes.  One K step of the gfx950 scaled MFMA covers 128 columns of
+ * 16 rows; lane l of the wave supplies the scale byte of row l%16 and 32-column block
+ * l/16.  A 256-byte tile holds 16 rows x 512 columns (four K steps): word l for lane l,
+ * byte j of that word for K step j of the four.  Tiles are ordered by 512-column group
+ * first, then by 16-row block; row_blocks is the number of 16-row blocks the array was
+ * laid out for.  Offset of the byte of (row, 32-column group): */
+int64_t orc_mx_mfma_offset(int64_t row, int64_t group, int64_t row_blocks);
+/* Place row-major scales e8m0[rows][lds] (groups per row used) into that layout, group g
+ * of the input at layout group group_off + g; bytes of other positions are not written. */
+void orc_mx_scales_to_mfma(const uint8_t* e8m0, int64_t lds, int64_t rows, int64_t groups,
+                           int64_t group_off, int64_t row_blocks, uint8_t* out);
+
 /* ---- MXFP8 on the collective topologies (P2 Summary / Modes) ----------
  * Flat layout: n E4M3 bytes and n/32 E8M0 bytes; group g = values [32g, 32g+32). */
 void orc_ring_hop_mx(const uint8_t* v_in, const uint8_t* e_in, const uint16_t* local,

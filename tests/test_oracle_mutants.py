@@ -135,6 +135,18 @@ MUTANTS = [
      "",
      ["test_ring_hop_clamps_the_quotients_of_few_bit_subnormal_scales",
       "test_ring_allreduce_of_cancelling_partials_clamps_like_the_brute_force"]),
+    ("MFMA layout swaps the K step and the 32-column block",
+     "    int64_t lane = 16 * block + row % 16; /* the lane that supplies this byte */",
+     "    int64_t lane = 16 * step + row % 16; step = block;",
+     ["test_mx_mfma_layout_worked_offsets", "test_mx_mfma_layout_is_lane_words_of_k_steps"]),
+    ("MFMA layout orders tiles by row block first",
+     "    int64_t tile = kgroup * row_blocks + rblock;",
+     "    int64_t tile = rblock * row_blocks + kgroup;",
+     ["test_mx_mfma_layout_worked_offsets", "test_mx_mfma_layout_is_lane_words_of_k_steps"]),
+    ("MFMA layout puts a row's four blocks in adjacent lanes",
+     "    int64_t lane = 16 * block + row % 16; /* the lane that supplies this byte */",
+     "    int64_t lane = 4 * (row % 16) + block;",
+     ["test_mx_mfma_layout_worked_offsets", "test_mx_mfma_layout_is_lane_words_of_k_steps"]),
     ("E4M3 saturates to the NaN code", "return (uint8_t)(sign | 0x7E);",
      "return (uint8_t)(sign | 0x7F);", ["test_e4m3_encode_signed_zero_and_saturation"]),
 ]

@@ -600,6 +600,73 @@ def test_mx_slices_equal_concatenation_and_leave_the_rest_untouched():
 # E4M3 128-block comparison codec
 # ---------------------------------------------------------------------------------------
 
+def test_mx_mfma_layout_worked_offsets():
+    """Byte offsets of scales in the scaled-MFMA layout, worked by hand from the matrix
+    instruction's scale operand (tests/golden/mx_mfma_layout.txt)."""
+    cases = [rec["case"] for rec in goldens.read("mx_mfma_layout.txt")]
+    cases = [list(map(int, c)) for c in cases]
+    assert len(cases) == 14
+    for row, group, rb, off in cases:
+        assert oracle.mx_mfma_offset(row, group, rb) == off, (row, group, rb)
+
+
+def test_mx_mfma_layout_is_lane_words_of_k_steps():
+    """The layout read the way the GEMM reads it: in tile (512-column group q, row block p),
+    the 32-bit word of lane l holds, in byte j, the scale of row 16p + l%16 and 32-column
+    group 16q + 4j + l/16 -- the byte lane l supplies at K step j.  Distinct scale bytes
+    per (row, group) make every placement visible; whole tiles are covered exactly once."""
+    rows, groups, rb = 48, 48, 3
+    e = np.zeros((rows, groups), np.uint8)
+    ids = {}
+    for r in range(rows):
+        for g in range(groups):
+            ids[(r, g)] = (r * groups + g) % 251
+    # pairs with the same id sit far apart; compare through the id table
+    for (r, g), v in ids.items():
+        e[r, g] = v
+    out = np.full(oracle.mx_mfma_bytes(rows, 32 * groups), 0xFF, np.uint8)
+    assert out.size == 256 * 3 * 3
+    oracle.mx_scales_to_mfma(e, out, rb)
+    seen = 0
+    for q in range(groups // 16):
+        for p in range(rows // 16):
+            tile = out[256 * (q * rb + p): 256 * (q * rb + p) + 256]
+            for lane in range(64):
+                for j in range(4):
+                    r, g = 16 * p + lane % 16, 16 * q + 4 * j + lane // 16
+                    assert tile[4 * lane + j] == ids[(r, g)], (q, p, lane, j)
+                    seen += 1
+    assert seen == rows * groups == out.size
+    # and the read-back through the offset map is the input
+    assert np.array_equal(oracle.mx_scales_from_mfma(out, rows, groups, rb), e)
+
+
+def test_mx_slices_in_the_mfma_layout_equal_the_concatenation():
+    """Six staged slices whose scales go to the MFMA layout equal the one-call quantization
+    of the concatenation in that layout; positions no slice covers stay untouched, rows at
+    or above the live rows too (slices at 128-column offsets that split 512-column groups)."""
+    rows, cap, cols = 40, 48, 384
+    xs = [workloads.rows(4, j, 0, rows, cols) for j in range(6)]
+    total = 6 * cols
+    v1 = np.full((cap, total), 0xEE, np.uint8)
+    e1 = np.full(oracle.mx_mfma_bytes(cap, total), 0xEE, np.uint8)
+    for j, x in enumerate(xs):
+        oracle.quant_mx_slice_mfma(x, j * cols, v1, e1, cap)
+    cat = np.concatenate(xs, axis=1)
+    v2 = np.full((cap, total), 0xEE, np.uint8)
+    e2 = np.full(oracle.mx_mfma_bytes(cap, total), 0xEE, np.uint8)
+    oracle.quant_mx_slice_mfma(cat, 0, v2, e2, cap)
+    assert np.array_equal(v1, v2) and np.array_equal(e1, e2)
+    vr, er = oracle.quant_mx(cat)
+    assert np.array_equal(v1[:rows], vr)
+    assert np.array_equal(oracle.mx_scales_from_mfma(e1, rows, total // 32, 3), er)
+    written = np.zeros(e1.size, bool)
+    for r in range(rows):
+        for g in range(total // 32):
+            written[oracle.mx_mfma_offset(r, g, 3)] = True
+    assert np.all(e1[~written] == 0xEE) and np.all(v1[rows:] == 0xEE)
+
+
 def test_e4m3_b128_worked_examples():
     for rec in goldens.read("e4m3_b128_worked.txt"):
         x = goldens.padded_block(rec["x"], 128)
