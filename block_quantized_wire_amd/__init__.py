@@ -30,6 +30,8 @@ __all__ = [
     "bq_dequant_accum_mx", "bq_a2a_reduce_mx", "bq_allgather_dequant_mx",
     "bq_ring_allreduce_mx", "bq_a2a_allreduce_mx",
     "bq_quant_e4m3_b128", "bq_dequant_e4m3_b128",
+    "bq_mx_scale_mfma_bytes", "bq_quant_mx_slice_mfma", "bq_quant_mx_slice_mfma_f16",
+    "bq_dequant_mx_mfma", "bq_mm_mx_mfma",
     "bq_wire_bytes_b128", "bq_status_str", "bq_version",
 ]
 
@@ -80,6 +82,10 @@ _SIGS = {
     "bq_allgather_dequant_mx": [_I, _P, _P, _I64, _PP, _I, _P],
     "bq_ring_allreduce_mx": [_I, _I64, _PP, _P, _P, _PP, _P],
     "bq_a2a_allreduce_mx": [_I, _I64, _PP, _PP, _PP, _P, _P, _P, _PP, _P],
+    "bq_quant_mx_slice_mfma": [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _P],
+    "bq_quant_mx_slice_mfma_f16": [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _P],
+    "bq_dequant_mx_mfma": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
+    "bq_mm_mx_mfma": [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I64, _P],
     "bq_quant_e4m3_b128": [_P, _I64, _P, _P, _P],
     "bq_dequant_e4m3_b128": [_P, _P, _I64, _P, _P],
 }
@@ -104,6 +110,8 @@ def _L() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.bq_wire_bytes_b128.argtypes = [_I64]
         L.bq_wire_bytes_b128.restype = _I64
+        L.bq_mx_scale_mfma_bytes.argtypes = [_I64, _I64]
+        L.bq_mx_scale_mfma_bytes.restype = _I64
         L.bq_status_str.argtypes = [ctypes.c_int]
         L.bq_status_str.restype = ctypes.c_char_p
         L.bq_version.argtypes = []
@@ -324,6 +332,58 @@ def bq_mm_mx(xv, xe, wv, we, y, M: int | None = None, N: int | None = None,
     _check("bq_mm_mx", _L().bq_mm_mx(_ptr(xv), xv.stride(0), _ptr(xe), xe.stride(0), _ptr(wv),
                                     wv.stride(0), _ptr(we), we.stride(0), M, N, K, _ptr(y),
                                     y.stride(0), _stream(stream)))
+
+
+def bq_mx_scale_mfma_bytes(rows: int, cols: int) -> int:
+    """Bytes of the scaled-MFMA scale layout for rows x cols (-1 for invalid sizes)."""
+    return _L().bq_mx_scale_mfma_bytes(rows, cols)
+
+
+def bq_quant_mx_slice_mfma(x, col_off: int, v, e8m0, capacity_rows: int | None = None,
+                           total_cols: int | None = None, rows: int | None = None,
+                           cols: int | None = None, ldx: int | None = None,
+                           ldv: int | None = None, f16: bool = False, stream=None) -> None:
+    """Staged slice x (rows, cols) into columns [col_off, col_off+cols) of v and its scale
+    bytes into e8m0, the scaled-MFMA layout of capacity_rows x total_cols (defaults: v's
+    rows and columns)."""
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ldx = x.stride(0) if ldx is None else ldx
+    ldv = v.stride(0) if ldv is None else ldv
+    capacity_rows = v.shape[0] if capacity_rows is None else capacity_rows
+    total_cols = v.shape[1] if total_cols is None else total_cols
+    name = "bq_quant_mx_slice_mfma_f16" if f16 else "bq_quant_mx_slice_mfma"
+    _check(name, getattr(_L(), name)(_ptr(x), rows, cols, ldx, col_off, _ptr(v), ldv, total_cols,
+                                     _ptr(e8m0), capacity_rows, _stream(stream)))
+
+
+def bq_quant_mx_slice_mfma_f16(x, col_off: int, v, e8m0, **kw) -> None:
+    bq_quant_mx_slice_mfma(x, col_off, v, e8m0, f16=True, **kw)
+
+
+def bq_dequant_mx_mfma(v, e8m0, y, scale_rows: int | None = None, rows: int | None = None,
+                       cols: int | None = None, stream=None) -> None:
+    rows = y.shape[0] if rows is None else rows
+    cols = y.shape[1] if cols is None else cols
+    scale_rows = v.shape[0] if scale_rows is None else scale_rows
+    _check("bq_dequant_mx_mfma",
+           _L().bq_dequant_mx_mfma(_ptr(v), v.stride(0), _ptr(e8m0), scale_rows, rows, cols,
+                                  _ptr(y), y.stride(0), _stream(stream)))
+
+
+def bq_mm_mx_mfma(xv, xe, wv, we, y, xe_rows: int | None = None, we_rows: int | None = None,
+                  M: int | None = None, N: int | None = None, K: int | None = None,
+                  stream=None) -> None:
+    """bq_mm_mx with xe, we in the scaled-MFMA layout (laid out for xe_rows / we_rows rows,
+    default xv's and wv's row counts)."""
+    M = y.shape[0] if M is None else M
+    N = y.shape[1] if N is None else N
+    K = xv.shape[1] if K is None else K
+    xe_rows = xv.shape[0] if xe_rows is None else xe_rows
+    we_rows = wv.shape[0] if we_rows is None else we_rows
+    _check("bq_mm_mx_mfma",
+           _L().bq_mm_mx_mfma(_ptr(xv), xv.stride(0), _ptr(xe), xe_rows, _ptr(wv), wv.stride(0),
+                             _ptr(we), we_rows, M, N, K, _ptr(y), y.stride(0), _stream(stream)))
 
 
 def bq_mx_staging_bytes(capacity_rows: int, total_cols: int) -> tuple[int, int]:

@@ -721,6 +721,124 @@ bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t l
                                      as_stream(stream)));
 }
 
+// ---- MXFP8 scales in the scaled-MFMA layout --------------------------------------------------
+
+namespace {
+
+int64_t mfma_bytes(int64_t rows, int64_t cols) {
+    return 256 * ((rows + 15) / 16) * ((cols + 511) / 512);
+}
+
+bq_status quant_mx_slice_mfma(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                              int64_t col_off, uint8_t* v, int64_t ldv, int64_t total_cols,
+                              uint8_t* e8m0, int64_t capacity_rows, bool f16, void* stream) {
+    BQ_TRY(check_mx_shape(rows, cols));
+    if (col_off < 0 || col_off % kBlk != 0 || total_cols < 0 || total_cols % kBlk != 0 ||
+        capacity_rows < 0)
+        return BQ_ERR_SIZE;
+    if (col_off > total_cols || cols > total_cols - col_off || total_cols > ldv ||
+        rows > capacity_rows)
+        return BQ_ERR_BOUNDS;
+    if (rows == 0 || cols == 0)
+        return BQ_OK;
+    if (!x || !v || !e8m0)
+        return BQ_ERR_NULL;
+    if (ldx < cols || !extent_fits(rows, cols, ldx, 2) ||
+        !extent_fits(rows, cols, ldv, 1) || !extent_fits(capacity_rows, total_cols, ldv, 1))
+        return BQ_ERR_BOUNDS;
+    if (!aligned(x, 16) || !aligned(v, 16) || !aligned(e8m0, 16) || ldx % 8 != 0 || ldv % 16 != 0)
+        return BQ_ERR_ALIGN;
+    const Span xs = span(x, extent(rows, cols, ldx, 2));
+    const Span vs = span(v + col_off, extent(rows, cols, ldv, 1));
+    const Span es = span(e8m0, mfma_bytes(capacity_rows, total_cols));
+    if (overlaps(xs, vs) || overlaps(xs, es) || overlaps(vs, es))
+        return BQ_ERR_ALIAS;
+    return launched(bq::launch_quant_mx_mfma(x, rows, cols, ldx, v + col_off, ldv, e8m0,
+                                             (capacity_rows + 15) / 16, col_off / kBlk,
+                                             as_stream(stream), f16));
+}
+
+}  // namespace
+
+int64_t bq_mx_scale_mfma_bytes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0 || cols % kBlk != 0 || rows > ((int64_t)1 << 40) ||
+        cols > ((int64_t)1 << 40))
+        return -1;
+    return mfma_bytes(rows, cols);
+}
+
+bq_status bq_quant_mx_slice_mfma(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 int64_t col_off, uint8_t* v, int64_t ldv, int64_t total_cols,
+                                 uint8_t* e8m0, int64_t capacity_rows, void* stream) {
+    return quant_mx_slice_mfma(x, rows, cols, ldx, col_off, v, ldv, total_cols, e8m0,
+                               capacity_rows, false, stream);
+}
+
+bq_status bq_quant_mx_slice_mfma_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                     int64_t col_off, uint8_t* v, int64_t ldv,
+                                     int64_t total_cols, uint8_t* e8m0, int64_t capacity_rows,
+                                     void* stream) {
+    return quant_mx_slice_mfma(x, rows, cols, ldx, col_off, v, ldv, total_cols, e8m0,
+                               capacity_rows, true, stream);
+}
+
+bq_status bq_dequant_mx_mfma(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
+                             int64_t scale_rows, int64_t rows, int64_t cols, uint16_t* y,
+                             int64_t ldy, void* stream) {
+    BQ_TRY(check_mx_shape(rows, cols));
+    if (scale_rows < 0)
+        return BQ_ERR_SIZE;
+    if (rows > scale_rows)
+        return BQ_ERR_BOUNDS;
+    if (rows == 0 || cols == 0)
+        return BQ_OK;
+    if (!v || !e8m0 || !y)
+        return BQ_ERR_NULL;
+    if (ldy < cols || ldv < cols || !extent_fits(rows, cols, ldy, 2) ||
+        !extent_fits(rows, cols, ldv, 1) || !extent_fits(scale_rows, cols, cols, 1))
+        return BQ_ERR_BOUNDS;
+    if (!aligned(y, 16) || !aligned(v, 16) || !aligned(e8m0, 16) || ldy % 8 != 0 || ldv % 16 != 0)
+        return BQ_ERR_ALIGN;
+    const Span ys = span(y, extent(rows, cols, ldy, 2));
+    if (overlaps(ys, span(v, extent(rows, cols, ldv, 1))) ||
+        overlaps(ys, span(e8m0, mfma_bytes(scale_rows, cols))))
+        return BQ_ERR_ALIAS;
+    return launched(bq::launch_dequant_mx_mfma(v, ldv, e8m0, (scale_rows + 15) / 16, rows, cols,
+                                               y, ldy, as_stream(stream)));
+}
+
+bq_status bq_mm_mx_mfma(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t xe_rows,
+                        const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t we_rows,
+                        int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,
+                        void* stream) {
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if (M < 0 || N < 0 || K <= 0 || K % kBlk != 0 || M > lim || N > lim || K > lim ||
+        xe_rows < 0 || we_rows < 0 || xe_rows > lim || we_rows > lim)
+        return BQ_ERR_SIZE;
+    if (xe_rows < M || we_rows < N)
+        return BQ_ERR_BOUNDS;
+    if (M == 0 || N == 0)
+        return BQ_OK;
+    if (!xv || !xe || !wv || !we || !y)
+        return BQ_ERR_NULL;
+    if (ldxv < K || ldwv < K || ldy < N)
+        return BQ_ERR_BOUNDS;
+    if (!extent_fits(M, K, ldxv, 1) || !extent_fits(N, K, ldwv, 1) || !extent_fits(M, N, ldy, 2))
+        return BQ_ERR_BOUNDS;
+    if (!aligned(xv, 16) || !aligned(wv, 16) || ldxv % 16 != 0 || ldwv % 16 != 0 ||
+        !aligned(xe, 16) || !aligned(we, 16) || !aligned(y, 2))
+        return BQ_ERR_ALIGN;
+    const Span ys = span(y, extent(M, N, ldy, 2));
+    if (overlaps(ys, span(xv, extent(M, K, ldxv, 1))) ||
+        overlaps(ys, span(xe, mfma_bytes(xe_rows, K))) ||
+        overlaps(ys, span(wv, extent(N, K, ldwv, 1))) ||
+        overlaps(ys, span(we, mfma_bytes(we_rows, K))))
+        return BQ_ERR_ALIAS;
+    return launched(bq::launch_mm_mx_mfma(xv, ldxv, xe, (xe_rows + 15) / 16, wv, ldwv, we,
+                                          (we_rows + 15) / 16, M, N, K, y, ldy,
+                                          as_stream(stream)));
+}
+
 // ---- E4M3 128-block codec ------------------------------------------------------------------
 
 bq_status bq_quant_e4m3_b128(const uint16_t* x, int64_t n, uint8_t* v, float* scale,

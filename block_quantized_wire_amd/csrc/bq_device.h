@@ -325,6 +325,20 @@ __device__ __forceinline__ float e8m0_inv_scale(uint32_t byte) {
     return __uint_as_float((254u - byte) << 23);
 }
 
+// ---- MXFP8 scales in the scaled-MFMA operand order ----------------------------------------
+
+// Byte offset of the E8M0 scale of (row, K step of 128 columns, 32-column block of that step)
+// in the layout the GEMM's scaled matrix instruction reads: one K step of
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes from lane l the scale of row l%16 and 32-column
+// block l/16, so a 256-byte tile holds 16 rows x 4 K steps as 64 words (word l for lane l,
+// byte j for K step j of the four); tiles are ordered by group of 4 K steps, then by 16-row
+// block, of `rb` row blocks.
+__device__ __forceinline__ int64_t mfma_scale_offset(uint32_t row, uint32_t step, uint32_t block,
+                                                     int64_t rb) {
+    const int64_t tile = (int64_t)(step >> 2) * rb + (row >> 4);
+    return tile * 256 + 4 * (16 * block + (row & 15)) + (step & 3);
+}
+
 // ---- lane walk -----------------------------------------------------------------------
 
 // Lane bookkeeping of the flat kernels with 8 values per lane (one 128-value block per DPP

@@ -66,11 +66,26 @@ hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
                              int64_t rows, int64_t cols, uint16_t* y, int64_t ldy,
                              hipStream_t stream);
 
+// The same with the scales in the scaled-MFMA layout of `rb` 16-row blocks (base e_layout);
+// the matrix's column 0 is K step `step0` of the layout.
+hipError_t launch_quant_mx_mfma(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* v, int64_t ldv, uint8_t* e_layout, int64_t rb,
+                                int64_t step0, hipStream_t stream, bool f16 = false);
+hipError_t launch_dequant_mx_mfma(const uint8_t* v, int64_t ldv, const uint8_t* e_layout,
+                                  int64_t rb, int64_t rows, int64_t cols, uint16_t* y,
+                                  int64_t ldy, hipStream_t stream);
+
 // The dense MXFP8 GEMM Y = bf16(X W^T) (M, N >= 1; K a positive multiple of 128).
 hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t ldxe,
                         const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe,
                         int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,
                         hipStream_t stream);
+// The same GEMM with both operands' scales in the scaled-MFMA layout, of xrb and wrb
+// 16-row blocks.
+hipError_t launch_mm_mx_mfma(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t xrb,
+                             const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t wrb,
+                             int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,
+                             hipStream_t stream);
 
 // E4M3 128-block codec.
 hipError_t launch_quant_e4m3_b128(const uint16_t* x, uint8_t* v, float* s, int64_t n,

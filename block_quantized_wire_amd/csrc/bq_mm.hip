@@ -33,6 +33,11 @@
 // double-buffered LDS area (2 x 8 KB), a quarter of the requests; otherwise each step stages
 // its rows' 4 bytes with its operands.
 //
+// With the scales in the scaled-MFMA layout (256-byte tiles of 16 rows x 4 K steps, word l
+// for lane l, byte j for step j), a group's scales for the workgroup are 32 whole tiles: one
+// 16-byte global-to-LDS load per lane brings them in, for any K that is a multiple of 128,
+// and each lane then reads its own word of its fragment's tile.
+//
 // Tiles are handed out column-major, each XCD (every 8th workgroup) taking a contiguous
 // run: an XCD works through a band of W columns, whose tiles all its workgroups re-read
 // from its own L2, while the X rows (the smaller operand) are shared by all XCDs through
@@ -57,13 +62,18 @@ constexpr int kScaleRows = kTM / kWaves;                 // scale rows per wave 
 constexpr int kGroupSteps = 4;                           // K steps per grouped scale load
 constexpr int kScaleSlots = kTM + kTN;                   // X rows, then W rows
 
+// How the E8M0 scales reach LDS: each K step its rows' 4 bytes from row-major rows; four
+// K steps at once, 16 bytes per row-major row; or four K steps at once as whole tiles of
+// the scaled-MFMA layout.
+enum Scales { kStepRows = 0, kGroupRows = 1, kGroupMfma = 2 };
+
 struct MmArgs {
     const uint8_t* xv;
     const uint8_t* xe;
     const uint8_t* wv;
     const uint8_t* we;
     uint16_t* y;
-    int64_t ldxv, ldxe, ldwv, ldwe, ldy;
+    int64_t ldxv, ldxe, ldwv, ldwe, ldy;   // MFMA layout: ldxe / ldwe are the 16-row blocks
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;   // row and column tiles
 };
@@ -79,9 +89,11 @@ struct Stage {
 struct Smem {
     Stage stage[2];
     // grouped scales: slot r (X row r, then W row r - kTM) holds the 16 E8M0 bytes of
-    // kGroupSteps K steps, word j for step j of the group
+    // kGroupSteps K steps, word j for step j of the group; in the MFMA layout the same
+    // area holds 32 tiles of 64 words (X row blocks 0..15, then W row blocks 0..15)
     uint32_t scg[2][kScaleSlots * kGroupSteps];
 };
+static_assert(kScaleSlots * kGroupSteps == 32 * 64, "a group of MFMA-layout tiles fills the area");
 
 __device__ __forceinline__ uint32_t x_scale_word(const Stage& st, int row) {
     return st.sc[(row / kScaleRows) * 64 + row % kScaleRows];
@@ -97,7 +109,7 @@ __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 
 // piece and fetches the chunk that belongs in that slot), and, in the per-step form, the
 // scale words of X and W rows [32w, 32w+32) (4 bytes per lane: lanes 0-31 X, 32-63 W).  Rows beyond M (N) are clamped to the last row; their
 // results are never stored.
-template <bool Grouped>
+template <int Sc>
 __device__ __forceinline__ void load_step(const MmArgs& p, Stage& st, int m0, int n0, int k0,
                                           int wave, int lane) {
 #pragma unroll
@@ -112,7 +124,7 @@ __device__ __forceinline__ void load_step(const MmArgs& p, Stage& st, int m0, in
         __builtin_amdgcn_global_load_lds(p.wv + (int64_t)nb * p.ldwv + k0 + 16 * c,
                                          st.b + piece * 1024, 16, 0, 0);
     }
-    if (Grouped)
+    if (Sc != kStepRows)
         return;
     const int r = kScaleRows * wave + (lane & 31);
     const uint8_t* src = lane < 32
@@ -131,6 +143,21 @@ __device__ __forceinline__ void load_scale_group(const MmArgs& p, uint32_t* dst,
         ? p.xe + (int64_t)min(m0 + slot, p.M - 1) * p.ldxe + 16 * g
         : p.we + (int64_t)min(n0 + slot - kTM, p.N - 1) * p.ldwe + 16 * g;
     __builtin_amdgcn_global_load_lds(src, dst + 64 * kGroupSteps * wave, 16, 0, 0);
+}
+
+// The scales of K steps [4g, 4g+4) from the scaled-MFMA layout into `dst`: the workgroup's
+// 16 X row blocks and 16 W row blocks are 32 tiles of 256 bytes; wave w fills tiles
+// [4w, 4w+4), 16 bytes per lane, lane i at byte 16i of the wave's 1 KB (tile 4w + i/16,
+// bytes [16(i%16), 16(i%16)+16) of it).  Row blocks beyond the last row are clamped to the
+// last one; their results are never stored.
+__device__ __forceinline__ void load_scale_group_mfma(const MmArgs& p, uint32_t* dst, int m0,
+                                                      int n0, int g, int wave, int lane) {
+    const int t = 4 * wave + (lane >> 4);
+    const int part = 16 * (lane & 15);
+    const uint8_t* src = t < 16
+        ? p.xe + ((int64_t)g * p.ldxe + min(m0 / 16 + t, (p.M - 1) / 16)) * 256 + part
+        : p.we + ((int64_t)g * p.ldwe + min(n0 / 16 + t - 16, (p.N - 1) / 16)) * 256 + part;
+    __builtin_amdgcn_global_load_lds(src, dst + 256 * wave, 16, 0, 0);
 }
 
 // Wait for this wave's global-to-LDS loads (the barrier that follows publishes them).
@@ -153,8 +180,9 @@ __device__ __forceinline__ int tile_of(int bid, int tiles) {
     return (bid % 8) * (tiles / 8) + bid / 8;
 }
 
-template <bool Grouped>
+template <int Sc>
 __global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
+    constexpr bool Grouped = Sc != kStepRows;
     __shared__ Smem sm;
     Stage* stage = sm.stage;
     const int tid = threadIdx.x;
@@ -173,37 +201,55 @@ __global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
             acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = p.K / kTK;
-    load_step<Grouped>(p, stage[0], m0, n0, 0, wave, lane);
-    if (Grouped)
+    load_step<Sc>(p, stage[0], m0, n0, 0, wave, lane);
+    if (Sc == kGroupRows)
         load_scale_group(p, sm.scg[0], m0, n0, 0, wave, lane);
+    if (Sc == kGroupMfma)
+        load_scale_group_mfma(p, sm.scg[0], m0, n0, 0, wave, lane);
     wait_loads();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more)
-            load_step<Grouped>(p, stage[(kt + 1) & 1], m0, n0, (kt + 1) * kTK, wave, lane);
+            load_step<Sc>(p, stage[(kt + 1) & 1], m0, n0, (kt + 1) * kTK, wave, lane);
         // the next group's scales go into the buffer the previous group used; they land by
         // this step's closing wait, three steps before they are read
-        if (Grouped && (kt & (kGroupSteps - 1)) == 0 && kt + kGroupSteps < nk)
-            load_scale_group(p, sm.scg[(kt / kGroupSteps + 1) & 1], m0, n0, kt / kGroupSteps + 1,
-                             wave, lane);
+        if (Grouped && (kt & (kGroupSteps - 1)) == 0 && kt + kGroupSteps < nk) {
+            uint32_t* next = sm.scg[(kt / kGroupSteps + 1) & 1];
+            if (Sc == kGroupRows)
+                load_scale_group(p, next, m0, n0, kt / kGroupSteps + 1, wave, lane);
+            else
+                load_scale_group_mfma(p, next, m0, n0, kt / kGroupSteps + 1, wave, lane);
+        }
         const Stage& st = stage[kt & 1];
         const uint32_t* scg = sm.scg[(kt / kGroupSteps) & 1] + (kt & (kGroupSteps - 1));
+        // MFMA layout: lane l's word of a fragment's tile, byte kt % 4
+        const uint32_t* tiles = sm.scg[(kt / kGroupSteps) & 1] + lane;
+        const int shift = 8 * (kt & (kGroupSteps - 1));
         i32x8 bf[kFB];
         int bsc[kFB];
 #pragma unroll
         for (int b = 0; b < kFB; ++b) {
             const int n = wn + 16 * b + r16;
             bf[b] = frag(st.b, n, g);
-            const uint32_t ww = Grouped ? scg[(kTM + n) * kGroupSteps] : w_scale_word(st, n);
-            bsc[b] = (int)((ww >> (8 * g)) & 0xFFu);
+            if constexpr (Sc == kGroupMfma) {
+                bsc[b] = (int)((tiles[64 * (16 + wn / 16 + b)] >> shift) & 0xFFu);
+            } else {
+                const uint32_t ww = Grouped ? scg[(kTM + n) * kGroupSteps] : w_scale_word(st, n);
+                bsc[b] = (int)((ww >> (8 * g)) & 0xFFu);
+            }
         }
 #pragma unroll
         for (int a = 0; a < kFA; ++a) {
             const int m = wm + 16 * a + r16;
             const i32x8 af = frag(st.a, m, g);
-            const uint32_t xw = Grouped ? scg[m * kGroupSteps] : x_scale_word(st, m);
-            const int asc = (int)((xw >> (8 * g)) & 0xFFu);
+            int asc;
+            if constexpr (Sc == kGroupMfma) {
+                asc = (int)((tiles[64 * (wm / 16 + a)] >> shift) & 0xFFu);
+            } else {
+                const uint32_t xw = Grouped ? scg[m * kGroupSteps] : x_scale_word(st, m);
+                asc = (int)((xw >> (8 * g)) & 0xFFu);
+            }
 #pragma unroll
             for (int b = 0; b < kFB; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -259,8 +305,32 @@ hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int6
     const bool grouped = K % (kTK * kGroupSteps) == 0 && reinterpret_cast<uintptr_t>(xe) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(we) % 16 == 0 && ldxe % 16 == 0 && ldwe % 16 == 0;
     if (grouped)
-        return launch1(k_mm_mx<true>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
-    return launch1(k_mm_mx<false>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
+        return launch1(k_mm_mx<kGroupRows>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
+    return launch1(k_mm_mx<kStepRows>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
+}
+
+hipError_t launch_mm_mx_mfma(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t xrb,
+                             const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t wrb,
+                             int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,
+                             hipStream_t stream) {
+    MmArgs a{};
+    a.xv = xv;
+    a.xe = xe;
+    a.wv = wv;
+    a.we = we;
+    a.y = y;
+    a.ldxv = ldxv;
+    a.ldxe = xrb;
+    a.ldwv = ldwv;
+    a.ldwe = wrb;
+    a.ldy = ldy;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    const int64_t tm = (M + kTM - 1) / kTM, tn = (N + kTN - 1) / kTN;
+    a.tiles_m = (int32_t)tm;
+    a.tiles_n = (int32_t)tn;
+    return launch1(k_mm_mx<kGroupMfma>, dim3((unsigned)(tm * tn)), dim3(kThreads), stream, a);
 }
 
 }  // namespace bq

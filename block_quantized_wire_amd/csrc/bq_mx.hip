@@ -45,8 +45,10 @@ struct FastDiv {
 struct MxArgs {
     const uint16_t* x;   // quantize input / dequantize output (as bf16 bits)
     uint8_t* v;
-    uint8_t* e;
+    uint8_t* e;          // row-major scales; or, in the MFMA layout, the layout's base
     int64_t ldx, ldv, lds;
+    int64_t rb;          // MFMA layout: its 16-row blocks
+    uint32_t step0;      // MFMA layout: the K step of the matrix's column 0
     uint32_t nblocks;    // rows * (cols / 128)
     FastDiv per_row;     // cols / 128
 };
@@ -99,7 +101,9 @@ struct Walk16 {
 // are one 16-byte store per lane.
 // F16: the input is IEEE binary16 (b12x pull request #241, Behavior: BF16 or FP16 slices);
 // the group byte then comes from the binary32 amax rule, which is exact for any amax.
-template <int U, bool F16>
+// Mfma: the scale bytes go to the scaled-MFMA layout (one byte store per lane pair) instead
+// of four bytes per 128 columns of a row-major scale row.
+template <int U, bool F16, bool Mfma = false>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
     const Walk16 w(U);
     const int lane = threadIdx.x & 63;
@@ -139,14 +143,20 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_mx(MxArgs a) {
             const uint32_t word = gather_e8m0_pairs(byte);
             if (ml[u].in) {
                 st16(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off, u32x4{lo.x, lo.y, hi.x, hi.y});
-                if ((lane & 7) == 0)
+                if constexpr (Mfma) {
+                    if ((lane & 1) == 0)
+                        a.e[mfma_scale_offset(ml[u].row, a.step0 + ml[u].cb, (lane & 7) >> 1, a.rb)] =
+                            (uint8_t)byte;
+                } else if ((lane & 7) == 0) {
                     *reinterpret_cast<uint32_t*>(a.e + ml[u].row * a.lds + ml[u].cb * 4) = word;
+                }
             }
         }
     }
 }
 
-template <int U>
+// Mfma: the scales are read from the scaled-MFMA layout.
+template <int U, bool Mfma = false>
 __global__ __launch_bounds__(kGroupThreads) void k_dequant_mx(MxArgs a) {
     const Walk w(U);
     const int grp = (threadIdx.x & 15) >> 2;
@@ -160,7 +170,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_dequant_mx(MxArgs a) {
         for (int u = 0; u < U; ++u) {
             ml[u] = mx_lane(a, t0 + u, w.sub);
             vv[u] = ml[u].in ? ld8(a.v + ml[u].row * a.ldv + ml[u].cb * kBlock + w.off) : u32x2{};
-            ev[u] = ml[u].in ? a.e[ml[u].row * a.lds + ml[u].cb * 4 + grp] : 127u;
+            if constexpr (Mfma)
+                ev[u] = ml[u].in ? a.e[mfma_scale_offset(ml[u].row, a.step0 + ml[u].cb, grp, a.rb)]
+                                 : 127u;
+            else
+                ev[u] = ml[u].in ? a.e[ml[u].row * a.lds + ml[u].cb * 4 + grp] : 127u;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -311,6 +325,41 @@ hipError_t launch_dequant_mx(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
     a.nblocks = (uint32_t)(rows * (cols / kBlock));
     a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
     return launch1(k_dequant_mx<kUMx>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads), stream, a);
+}
+
+hipError_t launch_quant_mx_mfma(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* v, int64_t ldv, uint8_t* e_layout, int64_t rb,
+                                int64_t step0, hipStream_t stream, bool f16) {
+    MxArgs a{};
+    a.x = x;
+    a.v = v;
+    a.e = e_layout;
+    a.ldx = ldx;
+    a.ldv = ldv;
+    a.rb = rb;
+    a.step0 = (uint32_t)step0;
+    a.nblocks = (uint32_t)(rows * (cols / kBlock));
+    a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
+    const dim3 grid(groups16_for<kUMxQ>(a.nblocks));
+    if (f16)
+        return launch1(k_quant_mx<kUMxQ, true, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_mx<kUMxQ, false, true>, grid, dim3(kGroupThreads), stream, a);
+}
+
+hipError_t launch_dequant_mx_mfma(const uint8_t* v, int64_t ldv, const uint8_t* e_layout,
+                                  int64_t rb, int64_t rows, int64_t cols, uint16_t* y,
+                                  int64_t ldy, hipStream_t stream) {
+    MxArgs a{};
+    a.x = y;
+    a.v = const_cast<uint8_t*>(v);
+    a.e = const_cast<uint8_t*>(e_layout);
+    a.ldx = ldy;
+    a.ldv = ldv;
+    a.rb = rb;
+    a.nblocks = (uint32_t)(rows * (cols / kBlock));
+    a.per_row = FastDiv::make((uint32_t)(cols / kBlock));
+    return launch1(k_dequant_mx<kUMx, true>, dim3(groups_for<kUMx>(a.nblocks)), dim3(kGroupThreads),
+                   stream, a);
 }
 
 hipError_t launch_quant_e4m3_b128(const uint16_t* x, uint8_t* v, float* s, int64_t n,

@@ -314,6 +314,56 @@ bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t l
                    const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe, int64_t M,
                    int64_t N, int64_t K, uint16_t* y, int64_t ldy, void* stream);
 
+/* ==== MXFP8 scales laid out for the scaled matrix instruction (P4 Behavior) ==========
+ *
+ * P4 Behavior has the caller-owned staging hold the MXFP8 values and the scale layout the
+ * dense GEMM consumes.  These entry points keep the values row-major as above and put the
+ * E8M0 bytes in the order gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes them: one K
+ * step of 128 columns of 16 rows takes from lane l the scale of row l%16 and 32-column
+ * block l/16.  The layout of a matrix with R rows (its row capacity) and C columns is
+ * ceil(R/16) * ceil(C/512) tiles of 256 bytes, tiles ordered by 512-column group first,
+ * then by 16-row block; in a tile, word l (bytes 4l..4l+3) belongs to lane l and its byte j
+ * to K step j of the group's four.  The scale of (row r, 32-column group g) therefore sits
+ * at byte 256 * ((g/16) * ceil(R/16) + r/16) + 4 * (16 * (g%4) + r%16) + (g%16)/4.
+ * Bytes of rows >= R or of columns >= C in a partial tile are never written or used.
+ * Layout arrays must be 16-byte aligned. */
+
+/* Bytes of the layout for rows x cols (cols a multiple of 128): 256 * ceil(rows/16) *
+ * ceil(cols/512).  Returns -1 for a negative size, cols not a multiple of 128, or a size
+ * beyond 2^40. */
+int64_t bq_mx_scale_mfma_bytes(int64_t rows, int64_t cols);
+
+/* Staged slice quantization with the scales in the layout: the bq_quant_mx_slice rule and
+ * value placement (columns [col_off, col_off+cols) of v, row stride ldv), and the slice's
+ * scale bytes at their layout positions in e8m0, a layout of capacity_rows rows and
+ * total_cols columns (bq_mx_scale_mfma_bytes(capacity_rows, total_cols) bytes).  Staged
+ * slices equal the one-call quantization of the concatenation in every byte (P4
+ * Validation).  cols, col_off, total_cols multiples of 128; col_off + cols <= total_cols
+ * <= ldv; rows <= capacity_rows; nothing outside the slice's values and scale bytes is
+ * written.  _f16: IEEE binary16 input (P4 Behavior: BF16 or FP16 slices). */
+bq_status bq_quant_mx_slice_mfma(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 int64_t col_off, uint8_t* v, int64_t ldv, int64_t total_cols,
+                                 uint8_t* e8m0, int64_t capacity_rows, void* stream);
+bq_status bq_quant_mx_slice_mfma_f16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                     int64_t col_off, uint8_t* v, int64_t ldv,
+                                     int64_t total_cols, uint8_t* e8m0, int64_t capacity_rows,
+                                     void* stream);
+
+/* bq_dequant_mx with the scales read from the layout: rows x cols of v (row stride ldv)
+ * whose scales are a layout of scale_rows (>= rows) rows starting at column 0. */
+bq_status bq_dequant_mx_mfma(const uint8_t* v, int64_t ldv, const uint8_t* e8m0,
+                             int64_t scale_rows, int64_t rows, int64_t cols, uint16_t* y,
+                             int64_t ldy, void* stream);
+
+/* bq_mm_mx with both operands' scales in the layout: xe laid out for xe_rows (>= M) rows,
+ * we for we_rows (>= N) rows, each holding at least K columns.  Same result bits as
+ * bq_mm_mx on the same values and scales.  The kernel brings four K steps' scales in as
+ * whole tiles for any K that is a multiple of 128. */
+bq_status bq_mm_mx_mfma(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t xe_rows,
+                        const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t we_rows,
+                        int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,
+                        void* stream);
+
 /* ==== E4M3 128-block codec: the format the INT8 codec replaces (P1 Summary, Why) ==== */
 
 /* Same block and footprint as the INT8 codec (132 bytes per 128 values): scale =

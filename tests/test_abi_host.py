@@ -302,6 +302,42 @@ def test_mx_collective_errors():
     assert aa(0, n, parts, vsend, esend, None, A + 2 ** 26, A + 2 ** 27, routs, S) == NSRC
 
 
+def test_mx_mfma_layout_errors():
+    """The scaled-MFMA scale layout: its size helper, and the slice quantizer, the
+    dequantizer and the GEMM that use it reject bad sizes, bounds, alignment (the layout
+    must be 16-byte aligned) and overlaps before launching."""
+    f = L.bq_mx_scale_mfma_bytes
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert f(4096, 43008) == 256 * 256 * 84
+    assert f(17, 640) == 256 * 2 * 2 and f(0, 0) == 0 and f(16, 128) == 256
+    assert f(-1, 128) == -1 and f(16, 100) == -1 and f(16, -128) == -1
+    x, v, e = A, A + 2 ** 24, A + 2 ** 26
+    q = L.bq_quant_mx_slice_mfma
+    assert q(x, 64, 100, 256, 0, v, 512, 512, e, 64, S) == SIZE          # cols off the block
+    assert q(x, 64, 256, 256, 64, v, 512, 512, e, 64, S) == SIZE         # offset off the block
+    assert q(x, 64, 256, 256, 0, v, 512, 500, e, 64, S) == SIZE          # total off the block
+    assert q(x, 64, 256, 256, 384, v, 512, 512, e, 64, S) == BOUNDS      # past total_cols
+    assert q(x, 64, 256, 256, 0, v, 384, 512, e, 64, S) == BOUNDS        # total_cols > ldv
+    assert q(x, 65, 256, 256, 0, v, 512, 512, e, 64, S) == BOUNDS        # rows > capacity
+    assert q(x, 64, 256, 256, 0, v, 512, 512, None, 64, S) == NULL
+    assert q(x, 64, 256, 256, 0, v, 512, 512, e + 4, 64, S) == ALIGN    # layout not 16-aligned
+    assert q(x, 64, 256, 256, 0, v, 512, 512, v + 256, 64, S) == ALIAS   # layout over the values
+    d = L.bq_dequant_mx_mfma
+    y = A + 2 ** 27
+    assert d(v, 512, e, 16, 17, 256, y, 256, S) == BOUNDS                # rows > scale_rows
+    assert d(v, 512, e + 8, 32, 17, 256, y, 256, S) == ALIGN
+    assert d(v, 512, e, 32, 17, 250, y, 256, S) == SIZE
+    assert d(v, 512, y + 64, 32, 17, 256, y, 256, S) == ALIAS
+    m = L.bq_mm_mx_mfma
+    xv, xe, wv, we, yy = A, A + 2 ** 24, A + 2 ** 25, A + 2 ** 26, A + 2 ** 27
+    assert m(xv, 512, xe, 32, wv, 512, we, 64, 33, 64, 512, yy, 64, S) == BOUNDS   # xe_rows < M
+    assert m(xv, 512, xe, 64, wv, 512, we, 32, 33, 64, 512, yy, 64, S) == BOUNDS   # we_rows < N
+    assert m(xv, 512, xe, 64, wv, 512, we, 64, 33, 64, 500, yy, 64, S) == SIZE
+    assert m(xv, 512, xe + 4, 64, wv, 512, we, 64, 33, 64, 512, yy, 64, S) == ALIGN
+    assert m(xv, 512, xe, 64, wv, 512, yy + 128, 64, 33, 64, 512, yy, 64, S) == ALIAS
+
+
 def test_mx_f16_errors():
     rows, cols = 16, 512
     x, v, e = A, A + 2 ** 20, A + 2 ** 21
@@ -382,12 +418,18 @@ def test_every_entry_point_accepts_empty_input():
         "bq_a2a_allreduce_mx": lambda: L.bq_a2a_allreduce_mx(3, 0, two, two, two, None, q, e,
                                                              two, S),
         "bq_mm_mx": lambda: L.bq_mm_mx(p, 256, e, 8, q, 256, e, 8, 0, 64, 256, y, 64, S),
+        "bq_quant_mx_slice_mfma": lambda: L.bq_quant_mx_slice_mfma(p, 0, 128, 128, 128, q, 256,
+                                                                   256, e, 0, S),
+        "bq_quant_mx_slice_mfma_f16": lambda: L.bq_quant_mx_slice_mfma_f16(p, 5, 0, 0, 0, q, 0, 0,
+                                                                           e, 5, S),
+        "bq_dequant_mx_mfma": lambda: L.bq_dequant_mx_mfma(q, 256, e, 16, 0, 256, y, 256, S),
+        "bq_mm_mx_mfma": lambda: L.bq_mm_mx_mfma(p, 256, e, 16, q, 256, e, 64, 0, 64, 256, y, 64, S),
         "bq_quant_e4m3_b128": lambda: L.bq_quant_e4m3_b128(p, 0, q, e, S),
         "bq_dequant_e4m3_b128": lambda: L.bq_dequant_e4m3_b128(q, e, 0, y, S),
     }
     compute = [n for n in declared_symbols()
                if n not in ("bq_status_str", "bq_version", "bq_wire_bytes_b128",
-                            "bq_mx_staging_bytes")]
+                            "bq_mx_staging_bytes", "bq_mx_scale_mfma_bytes")]
     assert sorted(calls) == compute
     for name, call in calls.items():
         assert call() == OK, name
