@@ -84,14 +84,12 @@ def code_only(text: str) -> str:
 
 
 def kernel_source_digest() -> str:
-    """Digest of the device code (the .hip sources and the headers they include, comments
-    left out): the HBM counters in profiles/ stay valid while it is unchanged; host-side
-    validation and comments may change."""
+    """Digest of the device code of the metric's kernels -- the INT8 kernels' source and the
+    headers it includes, comments left out: the HBM counters in profiles/ stay valid while it
+    is unchanged; host-side validation, comments and other kernel families may change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_wire_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".h")):
-            continue
+    for name in ("bq_device.h", "bq_i8.hip", "bq_launch.h"):
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode() + code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -313,39 +311,6 @@ def time_kernels(region: Region, seqs, reps: int, samples: int) -> dict:
     return out
 
 
-def metric_split(torch, region: Region, step, passes: int) -> dict:
-    """The metric's pass with a HIP event before every launch and after the last: each
-    kernel's duration inside the pipeline (its inputs as the previous kernel left them),
-    averaged over `passes` passes, and the region's total against the plain region."""
-    calls = step.metric
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls[0]) + 1)]
-          for _ in range(passes)]
-
-    def launch():
-        for i in range(passes):
-            for j, c in enumerate(calls[i % len(calls)]):
-                ev[i][j].record(region.stream)
-                run_calls([c])
-            ev[i][-1].record(region.stream)
-    region.time_us(launch)
-    per_pos = [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(passes)]
-               for j in range(len(calls[0]))]
-    kernels = {}
-    for j, (name, nbytes, _, _) in enumerate(calls[0]):
-        kernels.setdefault(f"{name} ({nbytes} B)", []).extend(per_pos[j])
-    out = {"kernels": {}, "positions_us": [round(statistics.mean(p), 2) for p in per_pos],
-           "pass_us": round(sum(statistics.mean(p) for p in per_pos), 2)}
-    for key, ds in kernels.items():
-        nbytes = int(key.rsplit("(", 1)[1].split()[0])
-        us = statistics.mean(ds)
-        gbs = nbytes / (us * 1e-6) / 1e9
-        n = len(ds) // passes
-        out["kernels"][key] = {"bytes_per_launch": nbytes, "launches_per_pass": n,
-                               "us_per_launch": round(us, 2), "us_per_pass": us * n,
-                               "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    return out
-
-
 def rate(nbytes: int, values: int, us: float) -> dict:
     """A pass's throughput as GB/s and as values per second, each against the HBM peak
     (the values-per-second bound is the peak over the pass's bytes per value)."""
@@ -514,45 +479,62 @@ MM_M, MM_N, MM_SLICES = 4096, 7168, 6      # staged projection: six 4096 x 7168 
 MFMA_FP8_PEAK_TFLOPS = 5000.0               # MI355X dense fp8 matrix-core peak
 
 
-def gemm_bench(torch, bq, reps: int, warmup: int = 2) -> dict:
-    """The dense MXFP8 GEMM from a staged buffer (not part of the step): six bf16 slices
-    of 4096 x 7168 quantized into a 4096 x 43008 staging buffer, times 7168 x 43008 MXFP8
-    weights, into bf16.  Synthetic N(0, 1) inputs drawn on the GPU with a fixed seed."""
+def gemm_bench(torch, bq, region: Region, reps: int, warmup: int = 20) -> dict:
+    """The dense MXFP8 GEMM from a staged buffer (not part of the step): six bf16 slices of
+    4096 x 7168 quantized into a 4096 x 43008 staging buffer, times 7168 x 43008 MXFP8
+    weights, into bf16.  Synthetic N(0, 1) inputs drawn on the GPU with a fixed seed.  Two
+    scale layouts are timed on the same values: row-major E8M0 rows (bq_mm_mx) and the
+    scaled-MFMA layout (bq_mm_mx_mfma), each at K = 43008 and at K = 42880, a K that is not
+    a multiple of 512; samples are taken round-robin over the four, after `warmup` launches
+    of each.  The headline figure is the staged layout the slice quantizer writes for the
+    GEMM, the MFMA layout, at K = 43008."""
     K = MM_SLICES * COLS
     g = torch.Generator(device="cuda")
     g.manual_seed(1234)
     xv = torch.empty((MM_M, K), dtype=torch.uint8, device="cuda")
     xe = torch.empty((MM_M, K // 32), dtype=torch.uint8, device="cuda")
+    xl = torch.empty(bq.bq_mx_scale_mfma_bytes(MM_M, K), dtype=torch.uint8, device="cuda")
     for j in range(MM_SLICES):
         xs = torch.randn((MM_M, COLS), generator=g, device="cuda").to(torch.bfloat16)
         bq.bq_quant_mx_slice(xs, j * COLS, xv, xe)
+        bq.bq_quant_mx_slice_mfma(xs, j * COLS, xv, xl)
     w = torch.randn((MM_N, K), generator=g, device="cuda").to(torch.bfloat16)
     wv = torch.empty((MM_N, K), dtype=torch.uint8, device="cuda")
     we = torch.empty((MM_N, K // 32), dtype=torch.uint8, device="cuda")
+    wl = torch.empty(bq.bq_mx_scale_mfma_bytes(MM_N, K), dtype=torch.uint8, device="cuda")
     bq.bq_quant_mx(w, wv, we)
+    bq.bq_quant_mx_slice_mfma(w, 0, wv, wl)
     del w
     y = torch.empty((MM_M, MM_N), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        bq.bq_mm_mx(xv, xe, wv, we, y)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    samples = []
+    runs = {
+        ("row-major", K): lambda: bq.bq_mm_mx(xv, xe, wv, we, y, K=K),
+        ("mfma", K): lambda: bq.bq_mm_mx_mfma(xv, xl, wv, wl, y, K=K),
+        ("row-major", K - 128): lambda: bq.bq_mm_mx(xv, xe, wv, we, y, K=K - 128),
+        ("mfma", K - 128): lambda: bq.bq_mm_mx_mfma(xv, xl, wv, wl, y, K=K - 128),
+    }
+    for fn in runs.values():
+        for _ in range(warmup):
+            fn()
+    samples = {key: [] for key in runs}
     for _ in range(SAMPLES):
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            bq.bq_mm_mx(xv, xe, wv, we, y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        samples.append(e0.elapsed_time(e1) * 1e3 / reps)
-    us = statistics.median(samples)
-    flops = 2.0 * MM_M * MM_N * K
-    tflops = flops / (us * 1e-6) / 1e12
-    return {"workload": f"staged MXFP8 GEMM {MM_M}x{MM_N}x{K} (six 4096x7168 slices), bf16 out",
-            "bound": "mfma", "us_per_launch": round(us, 1), "achieved": round(tflops, 1),
-            "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-            "flops_per_launch": flops, "samples_us": [round(t, 1) for t in samples]}
+        for key, fn in runs.items():
+            samples[key].append(region.time_us(lambda fn=fn: [fn() for _ in range(reps)]) / reps)
+    out = {}
+    for (layout, k), ss in samples.items():
+        us = statistics.median(ss)
+        flops = 2.0 * MM_M * MM_N * k
+        tflops = flops / (us * 1e-6) / 1e12
+        out[f"{layout} K={k}"] = {"us_per_launch": round(us, 1), "achieved": round(tflops, 1),
+                                  "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+                                  "flops_per_launch": flops,
+                                  "samples_us": [round(t, 1) for t in ss]}
+    head = out[f"mfma K={K}"]
+    return {"workload": f"staged MXFP8 GEMM {MM_M}x{MM_N}x{K} (six 4096x7168 slices), bf16 out, "
+                        "scales in the scaled-MFMA layout",
+            "bound": "mfma", "us_per_launch": head["us_per_launch"], "achieved": head["achieved"],
+            "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],
+            "flops_per_launch": head["flops_per_launch"], "samples_us": head["samples_us"],
+            "layouts": out}
 
 
 def copy_reference(torch, region: Region, total_bytes: int, reps: int) -> dict:
@@ -875,7 +857,6 @@ def main() -> int:
     metric_us = [region.time_us(lambda: [step.run_metric(i) for i in range(K)]) / K
                  for _ in range(SAMPLES)]
     metric = rate(step.metric_bytes, W * N, statistics.median(metric_us))
-    split = metric_split(torch, region, step, K)
 
     # each distinct kernel of the step alone: REPS back-to-back launches per sample
     per = time_kernels(region, step.kernels, REPS, SAMPLES)
@@ -883,9 +864,11 @@ def main() -> int:
         run_calls(seq)
     per_next = time_kernels(region, step.next_kernels, REPS, SAMPLES)
     # the roofline's kernel: the metric pass's kernel with the most time per pass, timed
-    # inside the metric's own region (events between its launches)
-    dom_name = max(split["kernels"], key=lambda k: split["kernels"][k]["us_per_pass"])
-    dom = split["kernels"][dom_name]
+    # alone with every input cold (events between launches inside the metric's region
+    # would add about 2.7 us per launch, a sixth of a hop)
+    metric_kernels = {f"{n} ({b} B)" for n, b, _, _ in step.metric[0]}
+    dom_name = max(metric_kernels, key=lambda k: per[k]["us_per_pass"])
+    dom = per[dom_name]
     copy_ref = copy_reference(torch, region, dom["bytes_per_launch"], REPS)
 
     # accuracy on input set 0, outside the timed regions: the all-reduce outputs against
@@ -953,8 +936,6 @@ def main() -> int:
                              samples_us=[round(t, 2) for t in metric_us],
                              values_counted="3072x7168 values quantized + 3 x 3072x7168 values "
                                             "hopped per pass"),
-        # the metric's kernels inside its region (events between launches), per launch
-        "value_split": split,
         # the whole step (every row of the hot path), timed region 1
         "step": {"workload": "4 simulated ranks x 3072x7168 bf16 partials, N(0,0.5): i8_ring + "
                              "i8_a2a all-reduce, MXFP8 staged slices + dequant, E4M3-b128 codec",
@@ -965,10 +946,8 @@ def main() -> int:
                      "bytes_per_launch": dom["bytes_per_launch"],
                      "us_per_launch": dom["us_per_launch"],
                      "launches_per_pass": dom["launches_per_pass"],
-                     "timed": "inside the metric's region: HIP events between its launches, "
-                              "K passes, the kernel's mean duration",
-                     # the same kernel alone, every input cold (per-kernel protocol below)
-                     "alone_cold": {kk: per[dom_name][kk] for kk in ("us_per_launch", "gbs", "frac")},
+                     "timed": "the kernel alone: REPS back-to-back launches over 16 buffer sets "
+                              "(every input cold), SAMPLES samples, median",
                      "traffic": traffic,
                      # a plain device copy of the same bytes per launch, timed the same way
                      "copy_same_bytes": dict(copy_ref, kernel_over_copy=round(
@@ -990,7 +969,7 @@ def main() -> int:
     if not args.no_configs:
         line["configs"] = config_bench(torch, bq, region, torch.cuda.current_stream(),
                                        CONFIG_PASSES, REPS)
-    line["gemm"] = gemm_bench(torch, bq, reps=4, warmup=20)
+    line["gemm"] = gemm_bench(torch, bq, region, reps=4)
     if not args.no_cpu_baseline:
         share = host_cpu_share()
         # repeats sized for about 10-20 s of CPU work in each of the three samples
