@@ -452,11 +452,15 @@ def build_configs(torch, bq, stream, which):
                             "E4M3 128-block codec on 16384x7168", n, calls, kern, keep)
 
 
-def config_bench(torch, bq, region: Region, stream, passes: int, reps: int) -> dict:
+CONFIGS = ["cfg1", "cfg3_w4", "cfg3_w16", "cfg4", "cfg5"]
+
+
+def config_bench(torch, bq, region: Region, stream, passes: int, reps: int,
+                 which=CONFIGS) -> dict:
     """Every configuration at full size: `passes` passes back to back (rotating buffer sets)
     as one timed region, and each of its kernels alone."""
     out = {}
-    for cr in build_configs(torch, bq, stream, ["cfg1", "cfg3_w4", "cfg3_w16", "cfg4", "cfg5"]):
+    for cr in build_configs(torch, bq, stream, which):
         for i in range(2 * len(cr.calls)):          # warm-up pass over every buffer set
             run_calls(cr.calls[i % len(cr.calls)])
         samples = []
@@ -810,6 +814,8 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the quantize, the hop and a copy from 8 MB to 1 GB per launch")
+    ap.add_argument("--config", choices=CONFIGS,
+                    help="only time one workload configuration at full size")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print a rocprofv3 kernel trace as a table and exit (no GPU needed)")
     args = ap.parse_args()
@@ -839,6 +845,10 @@ def main() -> int:
     region = Region(torch, torch.cuda.current_stream())
     if args.sweep:
         sweep(torch, bq, region)
+        return 0
+    if args.config:
+        print(json.dumps({"configs": config_bench(torch, bq, region, torch.cuda.current_stream(),
+                                                  CONFIG_PASSES, REPS, [args.config])}), flush=True)
         return 0
     step = Step(torch, bq, SETS)
     torch.cuda.synchronize()
