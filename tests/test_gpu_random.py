@@ -250,6 +250,58 @@ def test_random_mm_mx(seed):
     assert np.array_equal(host(y, np.uint16), want), "exact case differs"
 
 
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_mx_mfma_layout(seed):
+    """Staged slices with the scales in the scaled-MFMA layout (random rows, spare capacity,
+    slice count and widths, padded input rows, bf16 or binary16): values and every layout byte
+    against the oracle's map, bytes no slice owns untouched; then the GEMM reading the layout
+    (layouts laid out for more rows than M and N) against the GEMM reading row-major scales,
+    bit for bit."""
+    import torch
+    rng = np.random.default_rng(6000 + seed)
+    rows = int(rng.integers(1, 41))
+    cap = rows + int(rng.integers(0, 21))
+    widths = [blocks(rng, 1, 6) for _ in range(int(rng.integers(1, 5)))]
+    total = sum(widths) + 128 * int(rng.integers(0, 3))
+    fmt = "f16" if rng.integers(0, 2) else "bf16"
+    padx = 8 * int(rng.integers(0, 3))
+    say(f"random mx mfma layout seed={seed} {fmt} rows={rows} cap={cap} widths={widths} "
+        f"total={total} ldx pad {padx}")
+    ov = np.full((cap, total), 0xEE, np.uint8)
+    oe = np.full(oracle.mx_mfma_bytes(cap, total), 0xEE, np.uint8)
+    gv = filled((cap, total), np.uint8, 0xEE)
+    ge = filled(oracle.mx_mfma_bytes(cap, total), np.uint8, 0xEE)
+    off = 0
+    for w in widths:
+        x = draw(rng, rows * w, lo=-20, hi=14, fmt=fmt) if fmt == "f16" else draw(rng, rows * w)
+        x = x.reshape(rows, w)
+        xbuf = filled((rows, w + padx), np.uint16, 0xFF)
+        xbuf[:, :w].copy_(to_dev(x))
+        oracle.quant_mx_slice_mfma(x, off, ov, oe, cap, f16=fmt == "f16")
+        bq.bq_quant_mx_slice_mfma(xbuf[:, :w], off, gv, ge, capacity_rows=cap, total_cols=total,
+                                  rows=rows, cols=w, ldx=w + padx, f16=fmt == "f16")
+        off += w
+    sync()
+    assert_same(host(gv, np.uint8), ov, "staged values")
+    assert_same(host(ge, np.uint8), oe, "scale layout")
+    M, N = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    K = 128 * int(rng.integers(1, 17))
+    xrows, wrows = M + int(rng.integers(0, 40)), N + int(rng.integers(0, 40))
+    say(f"  gemm {M}x{N}x{K}, layouts for {xrows} and {wrows} rows")
+    xv, xe = oracle.quant_mx(draw(rng, M * K, lo=-30, hi=30).reshape(M, K))
+    wv, we = oracle.quant_mx(draw(rng, N * K, lo=-30, hi=30).reshape(N, K))
+    xl = np.full(oracle.mx_mfma_bytes(xrows, K), 0xFF, np.uint8)
+    wl = np.full(oracle.mx_mfma_bytes(wrows, K), 0xFF, np.uint8)
+    oracle.mx_scales_to_mfma(xe, xl, -(-xrows // 16))
+    oracle.mx_scales_to_mfma(we, wl, -(-wrows // 16))
+    y1, y2 = empty((M, N), np.uint16), empty((M, N), np.uint16)
+    dxv, dwv = to_dev(xv), to_dev(wv)
+    bq.bq_mm_mx(dxv, to_dev(xe), dwv, to_dev(we), y1)
+    bq.bq_mm_mx_mfma(dxv, to_dev(xl), dwv, to_dev(wl), y2, xe_rows=xrows, we_rows=wrows)
+    sync()
+    assert torch.equal(y1, y2), "scaled-MFMA layout GEMM differs from row-major scales"
+
+
 @pytest.mark.parametrize("nblocks", range(1, 18))
 def test_every_tile_residue(nblocks):
     """1..17 blocks: every residue of the block count modulo the 8-block tiles of the
