@@ -62,7 +62,8 @@ struct AccumArgs {
 };
 
 // A lane holds 16 values (Lanes16): its block's payload bytes are one 16-byte store.
-template <int U>
+// WT: the payload and scales are written through to the last-level cache (see st16_wt).
+template <int U, bool WT>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
     int8_t* __restrict__ q = a.q[blockIdx.y];
@@ -91,9 +92,13 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_i8(QuantArgs a) {
             const float sc = i8_scale(amax);
             const u32x2 lo = quant_i8x8(f, sc), hi = quant_i8x8(f + 8, sc);
             if (L.blk(u) < left) {
-                st16(q + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
-                if (L.leader)
-                    s[b0 + L.blk(u)] = sc;
+                st16_out<WT>(q + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
+                if (L.leader) {
+                    if constexpr (WT)
+                        st4_wt(s + b0 + L.blk(u), __float_as_uint(sc));
+                    else
+                        s[b0 + L.blk(u)] = sc;
+                }
             }
         }
     }
@@ -281,7 +286,10 @@ hipError_t launch_quant(int count, const uint16_t* const* x, int8_t* const* q,
         a.s[i] = s[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_quant_i8<kUQuant>, grid16_for<kUQuant>(a.nb, count), dim3(kGroupThreads), stream, a);
+    const dim3 grid = grid16_for<kUQuant>(a.nb, count);
+    if ((int64_t)count * a.nb * (kBlock + 4) <= kWriteThroughBytes)
+        return launch1(k_quant_i8<kUQuant, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_i8<kUQuant, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant(int count, const int8_t* const* q, const float* const* s,

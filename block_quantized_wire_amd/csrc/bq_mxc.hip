@@ -103,8 +103,8 @@ __device__ __forceinline__ void store_e8m0_word(uint8_t* p, uint32_t word) {
 }
 
 // A lane holds 16 values (Lanes16): a group of 32 is a lane pair, and the block's codes
-// are one 16-byte store per lane.
-template <int U>
+// are one 16-byte store per lane.  WT: written through to the last-level cache (st16_wt).
+template <int U, bool WT>
 __global__ __launch_bounds__(kGroupThreads) void k_quant_mxf(MxfQuantArgs a) {
     const uint16_t* __restrict__ x = a.x[blockIdx.y];
     uint8_t* __restrict__ v = a.v[blockIdx.y];
@@ -131,9 +131,13 @@ __global__ __launch_bounds__(kGroupThreads) void k_quant_mxf(MxfQuantArgs a) {
             const u32x2 lo = mx_encode8(f, byte), hi = mx_encode8(f + 8, byte);
             const uint32_t word = gather_e8m0_pairs(byte);
             if (L.blk(u) < left) {
-                st16(v + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
-                if (L.leader)
-                    store_e8m0_word(e + (b0 + L.blk(u)) * 4, word);
+                st16_out<WT>(v + b0 * kBlock + L.val(u), u32x4{lo.x, lo.y, hi.x, hi.y});
+                if (L.leader) {
+                    if constexpr (WT)
+                        st4_wt(e + (b0 + L.blk(u)) * 4, word);
+                    else
+                        store_e8m0_word(e + (b0 + L.blk(u)) * 4, word);
+                }
             }
         }
     }
@@ -316,7 +320,10 @@ hipError_t launch_quant(int count, const uint16_t* const* x, uint8_t* const* v,
         a.e[i] = e[i];
     }
     a.nb = n / kBlock;
-    return launch1(k_quant_mxf<kUMxfQ>, grid16_for<kUMxfQ>(a.nb, count), dim3(kGroupThreads), stream, a);
+    const dim3 grid = grid16_for<kUMxfQ>(a.nb, count);
+    if ((int64_t)count * a.nb * (kBlock + 4) <= kWriteThroughBytes)
+        return launch1(k_quant_mxf<kUMxfQ, true>, grid, dim3(kGroupThreads), stream, a);
+    return launch1(k_quant_mxf<kUMxfQ, false>, grid, dim3(kGroupThreads), stream, a);
 }
 
 hipError_t launch_dequant(int count, const uint8_t* const* v, const uint8_t* const* e,
