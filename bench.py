@@ -787,11 +787,12 @@ def summarize_trace(path: str) -> str:
         b2b = f"{statistics.mean(runs[k]):.2f}" if k in runs else ""
         lines.append(f"| `{k[0]}` | {k[1]} x {k[2]} | {len(ds)} | {statistics.mean(ds):.2f} | "
                      f"{min(ds):.2f} | {max(ds):.2f} | {b2b} | {100 * sum(ds) / total:.1f}% |")
-    q = ("k_quant_i8<1>", 1344, 4)
+    def is_quant(k):
+        return k[0].startswith("k_quant_i8<") and k[1:] == (1344, 4)
     h = ("k_ring_hop_i8<1>", 1344, 4)
     pos = [[], [], [], []]
     for i in range(len(keys) - 3):
-        if keys[i] == q and keys[i + 1] == h and keys[i + 2] == h and keys[i + 3] == h:
+        if is_quant(keys[i]) and keys[i + 1] == h and keys[i + 2] == h and keys[i + 3] == h:
             for p in range(4):
                 pos[p].append(dur[i + p])
     if pos[0]:
