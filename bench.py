@@ -31,6 +31,7 @@ work only, with no gap waiting for the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --sweep             (quantize, hop and copy from 8 MB to 1 GB)
+       python bench.py --gemm              (the staged MXFP8 GEMM alone)
        python bench.py --summarize-trace CSV   (rocprofv3 kernel trace -> table)
 """
 from __future__ import annotations
@@ -815,6 +816,9 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the quantize, the hop and a copy from 8 MB to 1 GB per launch")
+    ap.add_argument("--gemm", action="store_true",
+                    help="only time the staged MXFP8 GEMM (--steps launches per sample, at most 4; "
+                         "--warmup launches of each layout first)")
     ap.add_argument("--config", choices=CONFIGS,
                     help="only time one workload configuration at full size")
     ap.add_argument("--summarize-trace", metavar="CSV",
@@ -846,6 +850,10 @@ def main() -> int:
     region = Region(torch, torch.cuda.current_stream())
     if args.sweep:
         sweep(torch, bq, region)
+        return 0
+    if args.gemm:
+        print(json.dumps({"gemm": gemm_bench(torch, bq, region, reps=max(1, min(4, args.steps)),
+                                             warmup=args.warmup)}), flush=True)
         return 0
     if args.config:
         print(json.dumps({"configs": config_bench(torch, bq, region, torch.cuda.current_stream(),

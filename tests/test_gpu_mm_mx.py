@@ -183,3 +183,51 @@ def test_mm_mx_staged_full_size_sampled():
     B = block_max_sum(ov, oe, pv, pe)
     got = host(y, np.uint16)[np.ix_(rows, cols)]
     check_close(got, Y, S, B, K, "sampled outputs")
+
+
+@pytest.mark.parametrize("K", [384, 1024])
+def test_mm_mx_tile_widths_agree(K):
+    """The launcher picks 256- or 224-column tiles by how well they fill the compute units:
+    a 4096 x 4096 product takes 256-column tiles (16 x 16 tiles, one round on 256 units,
+    where 224-column tiles would make 304 and two rounds), and the same product computed in
+    224-column pieces takes 224-column tiles.  Every output is the same sum in the same
+    order either way, so the two agree bit for bit, for both scale layouts; sampled outputs
+    agree with the oracle.  K = 384 stages each step's scales with its operands, K = 1024
+    four steps at once."""
+    M = N = 4096
+    say(f"mm_mx tile widths {M}x{N}x{K}")
+    x = workloads.rows(4, 3, 0, M, K)
+    w = workloads.rows(6, 4, 0, N, K)
+    dx, dw = to_dev(x), to_dev(w)
+    xv, xe = empty((M, K), np.uint8), empty((M, K // 32), np.uint8)
+    wv, we = empty((N, K), np.uint8), empty((N, K // 32), np.uint8)
+    bq.bq_quant_mx(dx, xv, xe)
+    bq.bq_quant_mx(dw, wv, we)
+    xl = filled(bq.bq_mx_scale_mfma_bytes(M, K), np.uint8, 0xEE)
+    wl = filled(bq.bq_mx_scale_mfma_bytes(N, K), np.uint8, 0xEE)
+    bq.bq_quant_mx_slice_mfma(dx, 0, xv, xl)
+    bq.bq_quant_mx_slice_mfma(dw, 0, wv, wl)
+    whole = filled((M, N), np.uint16, 0x7F)
+    bq.bq_mm_mx(xv, xe, wv, we, whole)
+    whole_l = filled((M, N), np.uint16, 0x7F)
+    bq.bq_mm_mx_mfma(xv, xl, wv, wl, whole_l)
+    pieces = filled((M, N), np.uint16, 0x7F)
+    pieces_l = filled((M, N), np.uint16, 0x7F)
+    for c in range(0, N, 224):
+        n = min(224, N - c)
+        bq.bq_mm_mx(xv, xe, wv[c:c + n], we[c:c + n], pieces[:, c:c + n])
+        # a piece of the layout starts at its first 16-row block; the blocks per group stay N's
+        bq.bq_mm_mx_mfma(xv, xl, wv[c:c + n], wl[(c // 16) * 256:], pieces_l[:, c:c + n],
+                         we_rows=N)
+    sync()
+    assert torch.equal(whole, pieces), "256- and 224-column tiles differ (row-major scales)"
+    assert torch.equal(whole_l, pieces_l), "256- and 224-column tiles differ (MFMA layout)"
+    assert torch.equal(whole, whole_l), "the scale layouts give different products"
+    rng = np.random.default_rng(9)
+    rows = np.concatenate([[0, M - 1], rng.choice(M, 12, replace=False)])
+    cols = np.concatenate([[0, 223, 224, N - 1], rng.choice(N, 12, replace=False)])
+    ov, oe = oracle.quant_mx(np.ascontiguousarray(x[rows]))
+    pv, pe = oracle.quant_mx(np.ascontiguousarray(w[cols]))
+    Y, S = oracle.mm_mx(ov, oe, pv, pe)
+    got = host(whole, np.uint16)[np.ix_(rows, cols)]
+    check_close(got, Y, S, block_max_sum(ov, oe, pv, pe), K, "sampled outputs")
