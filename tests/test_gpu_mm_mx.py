@@ -185,16 +185,16 @@ def test_mm_mx_staged_full_size_sampled():
     check_close(got, Y, S, B, K, "sampled outputs")
 
 
-@pytest.mark.parametrize("K", [384, 1024])
-def test_mm_mx_tile_widths_agree(K):
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 384), (4096, 4096, 1024), (4000, 4000, 640)])
+def test_mm_mx_tile_widths_agree(M, N, K):
     """The launcher picks 256- or 224-column tiles by how well they fill the compute units:
     a 4096 x 4096 product takes 256-column tiles (16 x 16 tiles, one round on 256 units,
     where 224-column tiles would make 304 and two rounds), and the same product computed in
     224-column pieces takes 224-column tiles.  Every output is the same sum in the same
     order either way, so the two agree bit for bit, for both scale layouts; sampled outputs
-    agree with the oracle.  K = 384 stages each step's scales with its operands, K = 1024
-    four steps at once."""
-    M = N = 4096
+    agree with the oracle.  K = 384 and 640 stage each step's scales with its operands,
+    K = 1024 four steps at once; 4000 x 4000 leaves ragged row and column tiles (still 16 x 16
+    tiles of 256 against 16 x 18 of 224)."""
     say(f"mm_mx tile widths {M}x{N}x{K}")
     x = workloads.rows(4, 3, 0, M, K)
     w = workloads.rows(6, 4, 0, N, K)
@@ -225,7 +225,7 @@ def test_mm_mx_tile_widths_agree(K):
     assert torch.equal(whole, whole_l), "the scale layouts give different products"
     rng = np.random.default_rng(9)
     rows = np.concatenate([[0, M - 1], rng.choice(M, 12, replace=False)])
-    cols = np.concatenate([[0, 223, 224, N - 1], rng.choice(N, 12, replace=False)])
+    cols = np.concatenate([[0, 223, 224, 255, 256, N - 1], rng.choice(N, 12, replace=False)])
     ov, oe = oracle.quant_mx(np.ascontiguousarray(x[rows]))
     pv, pe = oracle.quant_mx(np.ascontiguousarray(w[cols]))
     Y, S = oracle.mm_mx(ov, oe, pv, pe)
