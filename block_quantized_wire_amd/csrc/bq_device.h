@@ -279,7 +279,9 @@ __device__ __forceinline__ void dequant_i8x8(u32x2 w, float s, float f[8]) {
 // 0): nearest code, ties to even, magnitudes above 448 saturate to 448, sign of zero kept.
 // The hardware conversion does this without a clamp below 464 (it gives NaN from there), and
 // every caller stays below 449: an MXFP8 group scale 2^e >= fl32(amax/448) leaves at most
-// 448 / (1 - 2^-24), and an E4M3-b128 quotient x / fl32(amax/448) at most 448 (1 + 2^-9).
+// 448 / (1 - 2^-24), and an E4M3-b128 quotient x / fl32(amax/448) of bf16 data at most
+// 2^16 / 146 = 448.88 (amax 2^-133, whose scale rounds down to 146 * 2^-149; a normal amax keeps it
+// within 448 (1 + 2^-23)).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
