@@ -143,6 +143,7 @@ class Step:
         P = lambda t: t.data_ptr()
         MB = M // 128
         self.calls, self.kernels, self.next_kernels, self.metric = [], [], [], []
+        self.share_kernels = []
         for b in self.sets:
             parts = b["parts"]
             calls, kern, nxt = [], [], []
@@ -226,9 +227,20 @@ class Step:
             nxt.append(("allgather_dequant_mx x4 skip own", NB * B_ALLGATHER_SKIP(W),
                         L.bq_allgather_dequant_mx,
                         (W, P(b["mx_bc_v"]), P(b["mx_bc_e"]), N, mouts, 1, sp)))
+            # one TP4 rank's share as its own single-segment launches: rank 0's step-0
+            # quantize of its 768x7168 chunk and its hop of the next chunk, in place
+            c1 = chunk(0, 1)
+            share = [("quant_i8 one rank", MB * B_QUANT, L.bq_quant_i8,
+                      (P(parts[0]) + 2 * M * chunk(0, 0), M, P(b["q_wire"]) + M * chunk(0, 0),
+                       P(b["s_wire"]) + 4 * MB * chunk(0, 0), sp)),
+                     ("ring_hop_i8 one rank", MB * B_HOP, L.bq_ring_hop_i8,
+                      (P(b["q_wire"]) + M * c1, P(b["s_wire"]) + 4 * MB * c1,
+                       P(parts[0]) + 2 * M * c1, M, P(b["q_wire"]) + M * c1,
+                       P(b["s_wire"]) + 4 * MB * c1, sp))]
             self.calls.append(calls)
             self.kernels.append(kern)
             self.next_kernels.append(nxt)
+            self.share_kernels.append(share)
             # the metric: the ring's step-0 quantize and its three hop steps
             self.metric.append(kern[:W])
         assert sum(c[1] for c in self.calls[0]) == sum(k[1] for k in self.kernels[0])
@@ -882,6 +894,7 @@ def main() -> int:
     for seq in step.next_kernels:           # the MXFP8 ring / all-to-all primitives
         run_calls(seq)
     per_next = time_kernels(region, step.next_kernels, REPS, SAMPLES)
+    per_share = time_kernels(region, step.share_kernels, REPS, SAMPLES)
     # the roofline's kernel: the metric pass's kernel with the most time per pass, timed
     # alone with every input cold (events between launches inside the metric's region
     # would add about 2.7 us per launch, a sixth of a hop)
@@ -979,6 +992,11 @@ def main() -> int:
         "next_kernels": {k: {kk: v[kk] for kk in ("bytes_per_launch", "launches_per_pass",
                                                   "us_per_launch", "gbs", "frac", "samples_us")}
                          for k, v in per_next.items()},
+        # one TP4 rank's share, 768x7168, as single-segment launches timed the same way
+        # (context: a launch this small pays its fixed start-up cost on 22 MB)
+        "share_kernels": {k: {kk: v[kk] for kk in ("bytes_per_launch", "us_per_launch", "gbs",
+                                                   "frac", "samples_us")}
+                          for k, v in per_share.items()},
     }
     line["accuracy"] = accuracy
     line["receipt"] = receipt(torch, bq)

@@ -61,6 +61,12 @@ def test_bench_line_fields():
                                     "row-major K=43008"]
     assert g["us_per_launch"] == g["layouts"]["mfma K=43008"]["us_per_launch"]
     assert d["accuracy"]["ranks_bit_identical"] is True
+    # one TP4 rank's share as single-segment launches: 43,008 blocks of 768x7168
+    sk = d["share_kernels"]
+    assert sk["quant_i8 one rank (16687104 B)"]["bytes_per_launch"] == 43008 * 388
+    assert sk["ring_hop_i8 one rank (22364160 B)"]["bytes_per_launch"] == 43008 * 520
+    for v in sk.values():
+        assert v["us_per_launch"] > 0 and abs(v["frac"] - v["gbs"] / 8000.0) < 1e-3
     # per-kernel figures are medians of their samples
     import statistics
     for k, v in d["kernels"].items():
