@@ -32,7 +32,7 @@ __all__ = [
     "bq_quant_e4m3_b128", "bq_dequant_e4m3_b128",
     "bq_mx_scale_mfma_bytes", "bq_quant_mx_slice_mfma", "bq_quant_mx_slice_mfma_f16",
     "bq_dequant_mx_mfma", "bq_mm_mx_mfma",
-    "bq_wire_bytes_b128", "bq_status_str", "bq_version",
+    "bq_wire_bytes_b128", "bq_mm_tile_cols", "bq_status_str", "bq_version",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libblockq.so")
@@ -112,6 +112,8 @@ def _L() -> ctypes.CDLL:
         L.bq_wire_bytes_b128.restype = _I64
         L.bq_mx_scale_mfma_bytes.argtypes = [_I64, _I64]
         L.bq_mx_scale_mfma_bytes.restype = _I64
+        L.bq_mm_tile_cols.argtypes = [_I64, _I64, ctypes.c_int]
+        L.bq_mm_tile_cols.restype = ctypes.c_int
         L.bq_status_str.argtypes = [ctypes.c_int]
         L.bq_status_str.restype = ctypes.c_char_p
         L.bq_version.argtypes = []
@@ -477,6 +479,12 @@ def bq_dequant_e4m3_b128(v, scale, y, n: int | None = None, stream=None) -> None
 
 
 # ---- host helpers --------------------------------------------------------------------------
+
+def bq_mm_tile_cols(M: int, N: int, cus: int) -> int:
+    """Column count (224 or 256) of the GEMM's workgroup tiles for M x N on `cus` compute
+    units (-1 for invalid sizes)."""
+    return _L().bq_mm_tile_cols(M, N, cus)
+
 
 def bq_wire_bytes_b128(n: int) -> int:
     return _L().bq_wire_bytes_b128(n)

@@ -721,6 +721,13 @@ bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t l
                                      as_stream(stream)));
 }
 
+int bq_mm_tile_cols(int64_t M, int64_t N, int cus) {
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if (M < 1 || N < 1 || M > lim || N > lim || cus < 1)
+        return -1;
+    return bq::mm_tile_cols(M, N, cus);
+}
+
 // ---- MXFP8 scales in the scaled-MFMA layout --------------------------------------------------
 
 namespace {

@@ -82,6 +82,9 @@ hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int6
                         hipStream_t stream);
 // The same GEMM with both operands' scales in the scaled-MFMA layout, of xrb and wrb
 // 16-row blocks.
+// The column count (256 or 224) of the GEMM's workgroup tiles for an M x N product on `cus`
+// compute units.
+int mm_tile_cols(int64_t M, int64_t N, int cus);
 hipError_t launch_mm_mx_mfma(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t xrb,
                              const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t wrb,
                              int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ldy,

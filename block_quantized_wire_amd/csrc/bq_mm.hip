@@ -320,27 +320,22 @@ __global__ __launch_bounds__(kThreads) void k_mm_mx(MmArgs p) {
     }
 }
 
-// The tile width for an M x N product: the one whose tiles fill the device's compute units
-// in the least time, counted as rounds of one workgroup per unit times the tile's width
-// (a 256 x 256 tile keeps a unit for 8/7 of a 256 x 224 tile's time); ties go to 256.
-int pick_tile_n(int64_t tm, int64_t N) {
+// The tile width the launches use on the current device (its compute-unit count read each
+// launch; 256 if it cannot be read).
+int pick_tile_n(int64_t M, int64_t N) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    const auto cost = [&](int64_t tn) {
-        const int64_t tiles = tm * ((N + tn - 1) / tn);
-        return (tiles + cus - 1) / cus * tn;
-    };
-    return cost(224) < cost(256) ? 224 : 256;
+    return mm_tile_cols(M, N, cus);
 }
 
 template <int Sc>
 hipError_t launch_tiled(const MmArgs& a0, hipStream_t stream) {
     MmArgs a = a0;
     const int64_t tm = (a.M + kTM - 1) / kTM;
-    const int tn_w = pick_tile_n(tm, a.N);
+    const int tn_w = pick_tile_n(a.M, a.N);
     const int64_t tn = (a.N + tn_w - 1) / tn_w;
     a.tiles_m = (int32_t)tm;
     a.tiles_n = (int32_t)tn;
@@ -351,6 +346,18 @@ hipError_t launch_tiled(const MmArgs& a0, hipStream_t stream) {
 }
 
 }  // namespace
+
+// The tile width for an M x N product on `cus` compute units: the one whose tiles fill the
+// units in the least time, counted as rounds of one workgroup per unit times the tile's
+// width (a 256 x 256 tile keeps a unit for 8/7 of a 256 x 224 tile's time); ties go to 256.
+int mm_tile_cols(int64_t M, int64_t N, int cus) {
+    const int64_t tm = (M + kTM - 1) / kTM;
+    const auto cost = [&](int64_t tn) {
+        const int64_t tiles = tm * ((N + tn - 1) / tn);
+        return (tiles + cus - 1) / cus * tn;
+    };
+    return cost(224) < cost(256) ? 224 : 256;
+}
 
 hipError_t launch_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t ldxe,
                         const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe,

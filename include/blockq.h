@@ -309,7 +309,9 @@ bq_status bq_a2a_allreduce_mx(int world, int64_t n, const uint16_t* const* parti
  * 4, with xe, we 4-byte aligned; ldy >= N; y must not overlap an input.
  * Speed, not results: when K is a multiple of 512 and xe, we are 16-byte aligned with ldxe,
  * ldwe divisible by 16, the kernel fetches four K steps' scale bytes per row at once (about
- * 6% faster at 4096 x 7168 x 43008); other layouts give the same bits. */
+ * 7% faster at 4096 x 7168 x 43008); other layouts give the same bits.  Workgroup tiles are
+ * 256 rows by 256 or 224 columns, whichever fills the device's compute units better
+ * (bq_mm_tile_cols); both give the same bits. */
 bq_status bq_mm_mx(const uint8_t* xv, int64_t ldxv, const uint8_t* xe, int64_t ldxe,
                    const uint8_t* wv, int64_t ldwv, const uint8_t* we, int64_t ldwe, int64_t M,
                    int64_t N, int64_t K, uint16_t* y, int64_t ldy, void* stream);
@@ -381,6 +383,12 @@ bq_status bq_dequant_e4m3_b128(const uint8_t* v, const float* scale, int64_t n, 
 /* Wire/staging bytes of n values in any 128-value block format: 132 * n / 128
  * (P1 Summary; P2 Summary).  Returns -1 if n is negative or not a multiple of 128. */
 int64_t bq_wire_bytes_b128(int64_t n);
+
+/* Column count of the dense MXFP8 GEMM's workgroup tiles (bq_mm_mx, bq_mm_mx_mfma) for an
+ * M x N product on a device with cus compute units: 224 or 256, whichever takes fewer
+ * rounds of one tile per unit times the tile width (ties to 256; the launches read the
+ * current device's count).  Returns -1 unless 1 <= M, N < 2^31 and cus >= 1. */
+int bq_mm_tile_cols(int64_t M, int64_t N, int cus);
 
 /* Static description of a status code. */
 const char* bq_status_str(bq_status status);

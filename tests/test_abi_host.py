@@ -51,6 +51,20 @@ def test_library_exports_every_declared_entry_point():
         assert hasattr(L, name), name
 
 
+def test_gemm_tile_width_rule():
+    """Rounds of one tile per compute unit times the tile width, the smaller wins, ties to 256."""
+    f = bq.bq_mm_tile_cols
+    assert f(4096, 7168, 256) == 224     # 512 tiles of 224 (2 rounds) against 448 of 256 (2 rounds)
+    assert f(4096, 4096, 256) == 256     # 256 tiles of 256 (1 round) against 304 of 224 (2)
+    assert f(4000, 4000, 256) == 256     # ragged: 16 x 16 against 16 x 18
+    assert f(1, 16, 256) == 224          # one round either way: the narrower tile is shorter
+    assert f(256, 1792, 1) == 256        # 8 tiles of 224 = 7 tiles of 256 in time: a tie
+    assert f(256, 1793, 1) == 224        # 9 x 224 = 2016 against 8 x 256 = 2048
+    assert f(4096, 7168, 304) == 224
+    for bad in ((0, 16, 256), (16, 0, 256), (1 << 31, 16, 256), (16, 1 << 31, 256), (16, 16, 0)):
+        assert f(*bad) == -1, bad
+
+
 def test_host_helpers():
     assert L.bq_wire_bytes_b128(128) == 132
     assert L.bq_wire_bytes_b128(512 * 7168) == 132 * 512 * 56
@@ -429,7 +443,7 @@ def test_every_entry_point_accepts_empty_input():
     }
     compute = [n for n in declared_symbols()
                if n not in ("bq_status_str", "bq_version", "bq_wire_bytes_b128",
-                            "bq_mx_staging_bytes", "bq_mx_scale_mfma_bytes")]
+                            "bq_mx_staging_bytes", "bq_mx_scale_mfma_bytes", "bq_mm_tile_cols")]
     assert sorted(calls) == compute
     for name, call in calls.items():
         assert call() == OK, name
