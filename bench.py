@@ -558,19 +558,19 @@ def copy_reference(torch, region: Region, total_bytes: int, reps: int) -> dict:
     """A plain device-to-device copy (torch's) moving total_bytes per launch, half read and half
     written: the rate a kernel of that many algorithmic bytes could reach if it did nothing but
     stream them.  Timed like the step's kernels: reps back-to-back launches on the same stream
-    between one pair of HIP events, the sources rotating over at least 1 GiB so they are cold in
-    the last-level cache."""
+    between one pair of HIP events, sources and destinations rotating over at least 1 GiB each,
+    so both are cold in the last-level cache (as the kernels' inputs and outputs are)."""
     half = total_bytes // 2
     nsrc = max(2, (1 << 30) // half + 1)
     src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsrc)]
-    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsrc)]
     with torch.cuda.stream(region.stream):
         for i in range(3):
-            dst[i % 2].copy_(src[i % nsrc])
+            dst[i % nsrc].copy_(src[i % nsrc])
 
         def launch():
             for i in range(reps):
-                dst[i % 2].copy_(src[(i + 3) % nsrc])
+                dst[(i + 3) % nsrc].copy_(src[(i + 3) % nsrc])
         us = statistics.median(region.time_us(launch) / reps for _ in range(3))
     del src, dst
     return {"bytes_per_launch": 2 * half, "us_per_launch": round(us, 2),
