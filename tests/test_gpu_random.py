@@ -356,3 +356,55 @@ def test_every_tile_residue(nblocks):
     assert_same(host(v2, np.uint8)[0, :n], fv, "MX 2-D codes")
     assert_same(host(e2, np.uint8)[0, :n // 32], fe, "MX 2-D scales")
     assert bool((v2[0, n:] == 0xA5).all()) and bool((e2[0, n // 32:] == 0xA5).all()), "MX 2-D wrote past cols"
+
+
+@pytest.mark.parametrize("seed", range(MM_CASES))
+def test_random_mm_wide_tiles(seed):
+    """Random ragged shapes the launcher runs on 256-column tiles (drawn until the device's
+    compute units make that the choice), K up to 1024: the product equals, bit for bit, the
+    same product computed in 224-column pieces (which take 224-column tiles), with row-major
+    and with MFMA-layout scales; a few outputs against the oracle's bound."""
+    from test_gpu_mm_mx import block_max_sum, check_close
+    import torch
+    rng = np.random.default_rng(8000 + seed)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for _ in range(200):
+        M, N = int(rng.integers(1, 4700)), int(rng.integers(2000, 4700))
+        if bq.bq_mm_tile_cols(M, N, cus) == 256:
+            break
+    else:
+        pytest.skip(f"no drawn shape takes 256-column tiles on {cus} compute units")
+    K = 128 * int(rng.integers(1, 9))
+    say(f"random mm wide tiles seed={seed} {M}x{N}x{K}")
+    x = draw(rng, M * K, lo=-30, hi=30).reshape(M, K)
+    w = draw(rng, N * K, lo=-30, hi=30).reshape(N, K)
+    dx, dw = to_dev(x), to_dev(w)
+    xv, xe = empty((M, K), np.uint8), empty((M, K // 32), np.uint8)
+    wv, we = empty((N, K), np.uint8), empty((N, K // 32), np.uint8)
+    bq.bq_quant_mx(dx, xv, xe)
+    bq.bq_quant_mx(dw, wv, we)
+    xl = filled(bq.bq_mx_scale_mfma_bytes(M, K), np.uint8, 0xEE)
+    wl = filled(bq.bq_mx_scale_mfma_bytes(N, K), np.uint8, 0xEE)
+    bq.bq_quant_mx_slice_mfma(dx, 0, xv, xl)
+    bq.bq_quant_mx_slice_mfma(dw, 0, wv, wl)
+    whole, whole_l = empty((M, N), np.uint16), empty((M, N), np.uint16)
+    bq.bq_mm_mx(xv, xe, wv, we, whole)
+    bq.bq_mm_mx_mfma(xv, xl, wv, wl, whole_l)
+    pieces, pieces_l = empty((M, N), np.uint16), empty((M, N), np.uint16)
+    for c in range(0, N, 224):
+        n = min(224, N - c)
+        assert bq.bq_mm_tile_cols(M, n, cus) == 224
+        bq.bq_mm_mx(xv, xe, wv[c:c + n], we[c:c + n], pieces[:, c:c + n])
+        bq.bq_mm_mx_mfma(xv, xl, wv[c:c + n], wl[(c // 16) * 256:], pieces_l[:, c:c + n],
+                         we_rows=N)
+    sync()
+    assert torch.equal(whole, pieces), "256- and 224-column tiles differ (row-major scales)"
+    assert torch.equal(whole_l, pieces_l), "256- and 224-column tiles differ (MFMA layout)"
+    assert torch.equal(whole, whole_l), "the scale layouts give different products"
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 6)]))
+    ov, oe = oracle.quant_mx(np.ascontiguousarray(x[rows]))
+    pv, pe = oracle.quant_mx(np.ascontiguousarray(w[cols]))
+    Y, S = oracle.mm_mx(ov, oe, pv, pe)
+    check_close(host(whole, np.uint16)[np.ix_(rows, cols)], Y, S, block_max_sum(ov, oe, pv, pe),
+                K, "sampled outputs")
