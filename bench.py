@@ -17,7 +17,8 @@ simulated ranks, each holding a 3072x7168 bf16 partial (N(0, 0.5)), go through
 fused ring-hop steps, timed as a region of its own (K passes back to back), as
 algorithmic bytes (each kernel's inputs read once, outputs written once) over time,
 in GB/s against the 8 TB/s HBM peak.  The whole step is reported beside it
-(`step`), and so is every distinct kernel of the step alone (`kernels`), each of
+(`step`), and so is every distinct kernel of the step alone (`kernels`), one TP4
+rank's own quantize and hop as single-segment launches (`share_kernels`), each of
 the five workload configurations at full size (`configs`) and the staged MXFP8
 GEMM (`gemm`).  Inputs are resident in HBM.  Sixteen complete buffer sets (inputs,
 intermediates, outputs; about 1.5 GB each) rotate pass by pass -- and launch by launch
