@@ -58,7 +58,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTM = 256, kTK = 128;                // workgroup tile rows, K step
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kWaveLoads = kTM * kTK / 1024 / kWaves;   // 1 KB loads per wave per operand
+constexpr int kWaveLoads = kTM * kTK / 1024 / kWaves;   // 1 KB X-tile loads per wave per step
 constexpr int kScaleRows = kTM / kWaves;                 // scale rows per wave per operand
 constexpr int kGroupSteps = 4;                           // K steps per grouped scale load
 constexpr int kScaleSlots = 2 * kTM;                     // X rows, then W rows
