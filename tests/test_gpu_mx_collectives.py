@@ -280,11 +280,25 @@ def test_mx_a2a_allreduce_small(W, rows):
         assert_same(host(outs[r], np.uint16), wouts[r], f"rank {r} output")
 
 
-@pytest.mark.parametrize("W", [4, 16])
-def test_mx_a2a_cfg3_sampled(W):
-    """4 and 16 ranks x 3072x7168: sampled rows of every owner's shard against the
-    oracle; every rank's full output bit-identical on the GPU; driver run without red."""
-    R = 3072
+def test_mx_a2a_cfg3_w4_full():
+    """4 ranks x 3072x7168: the broadcast payload and every rank's output against the
+    oracle in full (about ten seconds of oracle work), driver run without red."""
+    W = 4
+    say("mx a2a W=4 4x3072x7168 (full compare)")
+    parts = [workloads.tensor(3, r).reshape(-1) for r in range(W)]
+    _, vb, eb, outs = gpu_mx_a2a(parts, with_red=False)
+    _, wv, we, wouts = oracle.a2a_allreduce_mx(parts)
+    assert_same(host(vb, np.uint8), wv, "codes")
+    assert_same(host(eb, np.uint8), we, "bytes")
+    for r in range(W):
+        assert_same(host(outs[r], np.uint16), wouts[r], f"rank {r} output")
+
+
+def test_mx_a2a_cfg3_w16_sampled():
+    """16 ranks x 3072x7168: sampled rows of every owner's shard against the oracle (the
+    full MXFP8 oracle would take about half a minute on the host); every rank's full
+    output bit-identical on the GPU; driver run without red."""
+    R, W = 3072, 16
     say(f"mx a2a W={W} {W}x3072x7168 (sampled)")
     parts = [workloads.tensor(3, r) for r in range(W)]
     _, vb, eb, outs = gpu_mx_a2a(parts, with_red=False)
