@@ -323,17 +323,6 @@ def test_ring_allreduce_cfg2_full():
         assert_same(host(outs[r], np.uint16), wouts[r], f"rank {r} output")
 
 
-def _rows_per_chunk(total_rows: int, W: int, k: int, seed: int) -> np.ndarray:
-    """k sampled rows from each of the W chunks, in chunk order (so a sub-tensor made of
-    them keeps every sampled row in the chunk -- and ring order -- of its full tensor)."""
-    rng = np.random.default_rng(seed)
-    m = total_rows // W
-    rows = [np.sort(rng.choice(m, k, replace=False)) + c * m for c in range(W)]
-    rows[0][0] = 0
-    rows[-1][-1] = total_rows - 1
-    return np.concatenate(rows)
-
-
 def test_ring_allreduce_cfg5_prefill_full():
     """Prefill size: 4 ranks x 16384x7168 (t3, zero blocks, spikes): the final payloads and
     scales and every rank's output against the oracle in full (the oracle takes about ten
