@@ -92,7 +92,6 @@ def test_mx_f16_staged_slices_equal_one_call_and_oracle():
     assert_same(gv[:R], v1, "staged == one call (values)")
     assert_same(ge[:R], e1, "staged == one call (scales)")
     assert np.all(gv[R:] == 0xA5) and np.all(ge[R:] == 0x5A)
-    rows = np.array([0, 1, 77, 255, 300, 511])
-    wv, we = oracle.quant_mx_f16(np.ascontiguousarray(cat[rows]))
-    assert_same(gv[rows], wv, "sampled rows vs oracle (values)")
-    assert_same(ge[rows], we, "sampled rows vs oracle (scales)")
+    wv, we = oracle.quant_mx_f16(np.ascontiguousarray(cat))
+    assert_same(gv[:R], wv, "every row vs oracle (values)")
+    assert_same(ge[:R], we, "every row vs oracle (scales)")
